@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Throughput of the partition-attention hot path on one MI355X.
+
+A step is one pass of the whole hot path on the selective-reuse workload (long
+video DiT, B=1 H=24 D=128, 122880 keys in 32 partitions of 3840, a 3840-token
+query shard): at the anchor step, partition attention over all 32 partitions,
+their partition weights and the 28-way composition of the far partitions into a
+cached state; at the next step, partition attention over the 4 nearest
+partitions with the step's new inputs, the 5-way composition with the cached
+state and the 5-way weights. ``--config 2|3|4`` benches a single workload
+instead (all partitions, the P-way composition and the weights).
+
+Inputs are synthetic (seeded, see sequence_dit_amd/inputs.py) and resident in
+HBM before the timed region. Per-kernel times come from HIP events recorded on
+the launch stream inside the timed region. One JSON line is printed on stdout.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "partition-attn TFLOP/s (% bf16 MFMA peak) + as_merge GB/s (% HBM peak), 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "partition_attn_traffic.json")
+ATTN_SOURCE = os.path.join(ROOT, "sequence_dit_amd", "csrc", "partition_attn.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_digest(path=ATTN_SOURCE):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from the committed PMC capture, if it matches the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != source_digest():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+# --------------------------------------------------------------------------- #
+# CPU baseline: the oracle on a bounded sample of the same workload
+# --------------------------------------------------------------------------- #
+
+def cpu_baseline(w, target_s, reuse):
+    import numpy as np
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    nh = min(w.H, cores)
+    heads = list(range(nh))
+
+    def run(rows):
+        q = w.q[:, heads, :rows]
+        k, v = w.k[:, heads], w.v[:, heads]
+        t0 = time.perf_counter()
+        o, l = oracle.partition_states(q, k, v, w.ranges, w.scale, workers=cores)
+        oracle.contribution(l.reshape(w.P, -1), rows)
+        flops = 4 * nh * rows * w.D * sum(e - s for s, e in w.ranges)
+        if reuse:
+            near_ranges = [w.ranges[i] for i in w.near]
+            o1, l1 = oracle.partition_states(w.q1[:, heads, :rows], w.k1[:, heads], w.v1[:, heads], near_ranges,
+                                             w.scale, workers=cores)
+            full_o1 = np.zeros_like(o)
+            full_l1 = np.full_like(l, -np.inf)
+            full_o1[w.near], full_l1[w.near] = o1, l1
+            _, _, _, c_l = oracle.selective_reuse(o, l, full_o1, full_l1, w.near)
+            oracle.contribution(np.concatenate([l1, c_l[None]]).reshape(len(w.near) + 1, -1), rows)
+            flops += 4 * nh * rows * w.D * sum(e - s for s, e in near_ranges)
+        else:
+            oracle.merge(o, l)
+        return flops, time.perf_counter() - t0
+
+    # calibrate on two small samples (fixed cost + per-row cost), then run ~target_s seconds
+    _, ta = run(8)
+    _, tb = run(40)
+    per_row = max((tb - ta) / 32, 1e-6)
+    rows = int(max(8, min(w.Sq, (target_s - ta) / per_row + 8)))
+    flops, dt = run(rows)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{nh} of {w.H} heads x first {rows} of {w.Sq} query rows, all partitions of the step "
+                      f"(fp64 numpy, {dt:.1f} s)"}
+
+
+# --------------------------------------------------------------------------- #
+# GPU bench
+# --------------------------------------------------------------------------- #
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=5, choices=[2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): this library "
+              "models one device's share of sequence-parallel attention and has no multi-GPU path.",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    from sequence_dit_amd import _native as N
+    from sequence_dit_amd import inputs
+    from sequence_dit_amd.reuse import SelectiveReuse
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    N.lib()
+    dev = "cuda:0"
+    log(f"generating workload {args.config}")
+    w = inputs.make(args.config)
+    reuse = args.config == 5
+    q, k, v = w.q.to(dev), w.k.to(dev), w.v.to(dev)
+    if reuse:
+        q1, k1, v1 = w.q1.to(dev), w.k1.to(dev), w.v1.to(dev)
+        near = w.near
+    else:
+        near = list(range(w.P))  # unused
+    runner = SelectiveReuse(w.B, w.H, w.Sq, w.D, w.ranges, near, dev, w.scale)
+    all_idx = list(range(w.P))
+    merge_out = torch.empty((w.B, w.H, w.Sq, w.D), dtype=torch.float32, device=dev)
+    merge_lse = torch.empty((w.B, w.H, w.Sq), dtype=torch.float32, device=dev)
+
+    def step():
+        if reuse:
+            runner.anchor(q, k, v)
+            runner.step(q1, k1, v1)
+        else:
+            runner._timed("attn_anchor", N.partition_attn, q, k, v, w.ranges, w.scale,
+                          out=runner.state_out, lse=runner.state_lse)
+            runner._timed("contrib_anchor", runner._contribution, runner.state_lse, runner.anchor_weights,
+                          runner.anchor_scores)
+            runner._timed("merge_all", N.merge, [runner.state_out[i] for i in all_idx],
+                          [runner.state_lse[i] for i in all_idx], out=merge_out, lse=merge_lse)
+
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    runner.timer = []
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    ms_step = start.elapsed_time(end) / args.steps
+    log(f"timed region: {ms_step:.3f} ms/step (wall {wall_ms / args.steps:.3f} ms/step)")
+
+    times = {}
+    for name, s, e in runner.timer:
+        times.setdefault(name, []).append(s.elapsed_time(e))
+    rows = w.B * w.H * w.Sq
+    state_bytes = rows * (4 * w.D + 4)
+    per_key = 4 * w.B * w.H * w.Sq * w.D
+    attn_flops = {"attn_anchor": per_key * sum(e - s for s, e in w.ranges)}
+    attn_bytes = {"attn_anchor": 2 * w.B * w.H * (w.Sq * w.D + 2 * sum(e - s for s, e in w.ranges) * w.D)
+                  + w.P * state_bytes}
+    merges = {}
+    contribs = {"contrib_anchor": w.P}
+    if reuse:
+        fresh_keys = sum(w.ranges[i][1] - w.ranges[i][0] for i in near)
+        attn_flops["attn_fresh"] = per_key * fresh_keys
+        attn_bytes["attn_fresh"] = 2 * w.B * w.H * (w.Sq * w.D + 2 * fresh_keys * w.D) + len(near) * state_bytes
+        merges = {"merge_cached": w.P - len(near), "merge_step": len(near) + 1}
+        contribs["contrib_step"] = len(near) + 1
+    else:
+        merges = {"merge_all": w.P}
+
+    step_flops = sum(attn_flops.values())
+    attn_ms = sum(sum(times[n]) for n in attn_flops)
+    attn_launches = sum(len(times[n]) for n in attn_flops)
+    attn_total_flops = sum(attn_flops[n] * len(times[n]) for n in attn_flops)
+    achieved = attn_total_flops / (attn_ms * 1e-3) / 1e12
+    kernels = {}
+    for n in attn_flops:
+        ms = sum(times[n]) / len(times[n])
+        kernels[n] = {"ms": round(ms, 4), "TFLOP/s": round(attn_flops[n] / ms / 1e9, 1),
+                      "frac_mfma": round(attn_flops[n] / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+                      "GB/s_algorithmic": round(attn_bytes[n] / ms / 1e6, 1)}
+    merge_bytes_total, merge_ms_total = 0, 0.0
+    for n, kway in merges.items():
+        ms = sum(times[n]) / len(times[n])
+        by = (kway + 1) * state_bytes
+        merge_bytes_total += by * len(times[n])
+        merge_ms_total += sum(times[n])
+        kernels[n] = {"k": kway, "ms": round(ms, 4), "GB/s": round(by / ms / 1e6, 1),
+                      "frac_hbm": round(by / ms / 1e6 / PEAK_HBM_GBPS, 4)}
+    for n, P in contribs.items():
+        ms = sum(times[n]) / len(times[n])
+        by = 2 * P * rows * 4
+        kernels[n] = {"P": P, "ms": round(ms, 4), "GB/s": round(by / ms / 1e6, 1)}
+    merge_gbps = merge_bytes_total / (merge_ms_total * 1e-3) / 1e9
+
+    traffic = measured_traffic()
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "algorithmic_flops_per_launch": attn_total_flops / attn_launches,
+                "avg_launch_ms": round(attn_ms / attn_launches, 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(w, args.cpu_seconds, reuse)
+        log(f"cpu baseline {cpu['value']:.4f} TFLOP/s on {cpu['cores']} cores")
+
+    config = {"workload": w.name, "B": w.B, "H": w.H, "D": w.D, "Sq": w.Sq, "Skv": w.Skv, "P": w.P}
+    if reuse:
+        config.update({"fresh_partitions": near, "cached_partitions": w.P - len(near), "denoising_steps": 2})
+    line = {
+        "metric": METRIC,
+        "value": round(step_flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": config,
+        "merge_GBps": round(merge_gbps, 1),
+        "merge_frac_hbm": round(merge_gbps / PEAK_HBM_GBPS, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,197 @@
+"""ctypes binding of ``libas_attn.so`` (include/as_attn.h).
+
+Argument marshalling only: torch tensors become device pointers and sizes, the
+current torch HIP stream becomes the ``stream`` argument, and outputs are
+allocated with torch (caller-owned memory). Every step of the computation runs
+in the library's HIP kernels; there is no CPU fallback, and a missing library
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libas_attn.so")
+
+AS_OK, AS_ERR_INVALID_ARG, AS_ERR_UNSUPPORTED, AS_ERR_HIP = 0, 1, 2, 3
+AS_BF16, AS_F32 = 0, 1
+AS_MAX_PARTITIONS = 256
+AS_MAX_MERGE = 64
+
+EXPORTS = ("as_partition_attn", "as_merge", "as_partition_contribution_workspace_size",
+           "as_partition_contribution", "as_status_string", "as_last_error")
+
+_lib = None
+
+
+class ASError(RuntimeError):
+    """A call into the library returned a status other than AS_OK."""
+
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+STATUS_NAMES = {AS_OK: "AS_OK", AS_ERR_INVALID_ARG: "AS_ERR_INVALID_ARG",
+                AS_ERR_UNSUPPORTED: "AS_ERR_UNSUPPORTED", AS_ERR_HIP: "AS_ERR_HIP"}
+
+c_i64p = ctypes.POINTER(ctypes.c_int64)
+c_i32p = ctypes.POINTER(ctypes.c_int32)
+c_vpp = ctypes.POINTER(ctypes.c_void_p)
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library (once); raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library {LIB_PATH} is missing: build it with "
+                               "`python -m sequence_dit_amd.build` (or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        L.as_partition_attn.restype = ctypes.c_int
+        L.as_partition_attn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                        c_i64p, c_i64p, c_i32p, ctypes.c_int32, ctypes.c_float,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.as_merge.restype = ctypes.c_int
+        L.as_merge.argtypes = [ctypes.c_int32, c_vpp, c_vpp, ctypes.c_int64, ctypes.c_int64,
+                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.as_partition_contribution_workspace_size.restype = ctypes.c_size_t
+        L.as_partition_contribution_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int64]
+        L.as_partition_contribution.restype = ctypes.c_int
+        L.as_partition_contribution.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                                ctypes.c_void_p]
+        L.as_status_string.restype = ctypes.c_char_p
+        L.as_status_string.argtypes = [ctypes.c_int]
+        L.as_last_error.restype = ctypes.c_char_p
+        L.as_last_error.argtypes = []
+        _lib = L
+    return _lib
+
+
+def check(status: int) -> None:
+    if status != AS_OK:
+        raise ASError(status, lib().as_last_error().decode())
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _require_gpu(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must live on a HIP device; the library has no CPU path")
+
+
+def _i64(vals) -> ctypes.Array:
+    return (ctypes.c_int64 * len(vals))(*vals)
+
+
+# --------------------------------------------------------------------------- #
+# as_partition_attn
+# --------------------------------------------------------------------------- #
+
+def partition_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_ranges: Sequence[Tuple[int, int]],
+                   scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Attention states of q [B,H,Sq,D] against each range of k, v [B,H,Skv,D].
+
+    Returns OUT [P,B,H,Sq,D] and LSE [P,B,H,Sq] (float32), enqueued on the current stream.
+    """
+    _require_gpu(q, k, v)
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or k.stride() != v.stride():
+        raise ValueError("q must be [B,H,Sq,D]; k and v [B,H,Skv,D] with equal strides")
+    if q.dtype != k.dtype or k.dtype != v.dtype or q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q, k, v must share dtype bfloat16 or float32")
+    B, H, Sq, D = q.shape
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != D:
+        raise ValueError("q and k/v disagree on B, H or D")
+    if q.stride(3) != 1 or k.stride(3) != 1:
+        raise ValueError("the head dimension must be contiguous")
+    Skv = k.shape[2]
+    P = len(kv_ranges)
+    if out is None:
+        out = torch.empty((P, B, H, Sq, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((P, B, H, Sq), dtype=torch.float32, device=q.device)
+    if not (out.is_contiguous() and lse.is_contiguous() and out.dtype == torch.float32 and lse.dtype == torch.float32):
+        raise ValueError("out and lse must be contiguous float32")
+    if out.numel() != P * B * H * Sq * D or lse.numel() != P * B * H * Sq:
+        raise ValueError("out/lse have the wrong size")
+    flat = [int(x) for r in kv_ranges for x in r]
+    ranges = (ctypes.c_int32 * max(1, len(flat)))(*flat)
+    dt = AS_BF16 if q.dtype == torch.bfloat16 else AS_F32
+    sc = float(D ** -0.5 if scale is None else scale)
+    check(lib().as_partition_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), dt, B, H, Sq, Skv, D,
+                                  _i64(q.stride()[:3]), _i64(k.stride()[:3]), ranges, P, sc,
+                                  out.data_ptr(), lse.data_ptr(), _stream(q)))
+    return out, lse
+
+
+# --------------------------------------------------------------------------- #
+# as_merge
+# --------------------------------------------------------------------------- #
+
+def merge(outs: Sequence[torch.Tensor], lses: Sequence[torch.Tensor], out: Optional[torch.Tensor] = None,
+          lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Compose n states (OUT_k [..., D], LSE_k [...]) into one; returns (OUT, LSE)."""
+    n = len(outs)
+    if n != len(lses) or n == 0:
+        raise ValueError("need the same positive number of OUT and LSE tensors")
+    _require_gpu(*outs, *lses)
+    D = outs[0].shape[-1]
+    rows = outs[0].numel() // D
+    for o, l in zip(outs, lses):
+        if o.dtype != torch.float32 or l.dtype != torch.float32 or not o.is_contiguous() or not l.is_contiguous():
+            raise ValueError("states must be contiguous float32")
+        if o.numel() != rows * D or l.numel() != rows:
+            raise ValueError("states disagree in size")
+    if out is None:
+        out = torch.empty(outs[0].shape, dtype=torch.float32, device=outs[0].device)
+    if lse is None:
+        lse = torch.empty(lses[0].shape, dtype=torch.float32, device=outs[0].device)
+    optrs = (ctypes.c_void_p * n)(*[o.data_ptr() for o in outs])
+    lptrs = (ctypes.c_void_p * n)(*[l.data_ptr() for l in lses])
+    check(lib().as_merge(n, optrs, lptrs, rows, D, out.data_ptr(), lse.data_ptr(), _stream(outs[0])))
+    return out, lse
+
+
+# --------------------------------------------------------------------------- #
+# as_partition_contribution
+# --------------------------------------------------------------------------- #
+
+def contribution_workspace_size(P: int, rows: int, rows_per_group: int) -> int:
+    return int(lib().as_partition_contribution_workspace_size(P, rows, rows_per_group))
+
+
+def partition_contribution(lse: torch.Tensor, rows_per_group: int, want_weights: bool = True,
+                           want_scores: bool = True, workspace: Optional[torch.Tensor] = None):
+    """Per-row weights w [P, rows] and per-group scores [rows/rows_per_group, P] from LSE [P, ...]."""
+    _require_gpu(lse)
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32")
+    P = lse.shape[0]
+    rows = lse.numel() // max(P, 1)
+    w = torch.empty((P, rows), dtype=torch.float32, device=lse.device) if want_weights else None
+    s = None
+    ws_bytes = 0
+    if want_scores:
+        if rows_per_group < 1 or rows % rows_per_group:
+            raise ValueError("rows_per_group must divide the number of rows")
+        s = torch.empty((rows // rows_per_group, P), dtype=torch.float32, device=lse.device)
+        ws_bytes = contribution_workspace_size(P, rows, rows_per_group)
+        if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
+            workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=lse.device)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    check(lib().as_partition_contribution(lse.data_ptr(), P, rows, rows_per_group,
+                                          w.data_ptr() if w is not None else None,
+                                          s.data_ptr() if s is not None else None,
+                                          workspace.data_ptr() if workspace is not None else None,
+                                          ws_bytes, _stream(lse)))
+    return w, s

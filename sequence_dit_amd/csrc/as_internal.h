@@ -1,0 +1,62 @@
+// Internal launch interface between the C ABI layer (api.hip) and the kernels.
+// Not installed; the public interface is include/as_attn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "as_attn.h"
+
+namespace as {
+
+// Arguments of one partition-attention launch, passed by value as the kernel
+// argument (the key ranges travel in the kernarg segment).
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t q_sb, q_sh, q_ss;  // element strides of q over (b, h, s)
+  int64_t k_sb, k_sh, k_ss;  // element strides of k and v over (b, h, s)
+  float* out;                // [P][B][H][Sq][D]
+  float* lse;                // [P][B][H][Sq]
+  int32_t B, H, Sq, Skv, D, P;
+  int32_t n_qtiles;          // ceil(Sq / rows per workgroup)
+  float scale;               // softmax scale
+  float scale_log2;          // scale * log2(e)
+  int32_t ranges[2 * AS_MAX_PARTITIONS];
+};
+
+struct MergeArgs {
+  const float* outs[AS_MAX_MERGE];
+  const float* lses[AS_MAX_MERGE];
+  float* out;
+  float* lse;
+  int64_t rows;
+  int32_t n;
+  int32_t D;
+};
+
+struct ContribArgs {
+  const float* lse;   // [P][rows]
+  float* weights;     // [P][rows] or null
+  float* scores;      // [G][P] or null
+  float* partial;     // [G][chunks_per_group][P] workspace or null
+  int64_t rows;
+  int64_t rows_per_group;
+  int32_t P;
+  int32_t chunks_per_group;
+};
+
+// Rows of the query shard handled by one workgroup of the bf16 kernel.
+int attn_bf16_rows_per_block(int D);
+int attn_f32_rows_per_block(int D);
+
+hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+
+// Contribution: rows are processed in chunks of this many rows per workgroup.
+constexpr int kContribChunk = 256;
+hipError_t launch_contribution(const ContribArgs& a, hipStream_t stream);
+
+}  // namespace as

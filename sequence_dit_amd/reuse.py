@@ -1,0 +1,104 @@
+"""Selective attention-state reuse across denoising steps, as a sequence of library calls.
+
+DiTango review page (pith.science), "What carries the argument" and Fig. 6 caption:
+at an anchor step every partition's state is computed; the states of the
+remote (low-contribution) partitions are composed into one cached state; at the
+following steps only the near partitions are recomputed and composed with the
+cached state. The partition weights (Eq. 8, softmax of LSE over partitions) are
+refreshed at the anchor.
+
+Everything here is buffer management and ordering on the current torch stream;
+each step of the arithmetic runs in the HIP library (``_native``).
+"""
+from __future__ import annotations
+
+from typing import List, Sequence, Tuple
+
+import torch
+
+from . import _native
+
+
+class SelectiveReuse:
+    """Preallocated buffers and call order for one query shard against P partitions."""
+
+    def __init__(self, B: int, H: int, Sq: int, D: int, ranges: Sequence[Tuple[int, int]], near: Sequence[int],
+                 device, scale: float | None = None):
+        # optional list that receives (name, start_event, end_event) around every library call
+        self.timer: List | None = None
+        self.ranges = [tuple(r) for r in ranges]
+        self.P = len(self.ranges)
+        self.near = sorted(int(i) for i in near)
+        if not self.near or len(set(self.near)) != len(self.near) or not all(0 <= i < self.P for i in self.near):
+            raise ValueError("near must be distinct partition indices")
+        self.far = [i for i in range(self.P) if i not in set(self.near)]
+        self.rows = B * H * Sq
+        self.rows_per_group = Sq
+        self.scale = D ** -0.5 if scale is None else scale
+        f32 = dict(dtype=torch.float32, device=device)
+        nf = len(self.near)
+        # anchor: states of every partition
+        self.state_out = torch.empty((self.P, B, H, Sq, D), **f32)
+        self.state_lse = torch.empty((self.P, B, H, Sq), **f32)
+        # reuse step: fresh near states plus the cached composed state in the last slot
+        self.step_out = torch.empty((nf + 1, B, H, Sq, D), **f32)
+        self.step_lse = torch.empty((nf + 1, B, H, Sq), **f32)
+        self.result_out = torch.empty((B, H, Sq, D), **f32)
+        self.result_lse = torch.empty((B, H, Sq), **f32)
+        G = self.rows // self.rows_per_group
+        self.anchor_weights = torch.empty((self.P, self.rows), **f32)
+        self.anchor_scores = torch.empty((G, self.P), **f32)
+        self.step_weights = torch.empty((nf + 1, self.rows), **f32)
+        self.step_scores = torch.empty((G, nf + 1), **f32)
+        ws = max(_native.contribution_workspace_size(self.P, self.rows, self.rows_per_group),
+                 _native.contribution_workspace_size(nf + 1, self.rows, self.rows_per_group), 16)
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
+
+    @property
+    def cached_out(self) -> torch.Tensor:
+        return self.step_out[-1]
+
+    @property
+    def cached_lse(self) -> torch.Tensor:
+        return self.step_lse[-1]
+
+    def _timed(self, name: str, fn, *args, **kw):
+        if self.timer is None:
+            return fn(*args, **kw)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        r = fn(*args, **kw)
+        end.record()
+        self.timer.append((name, start, end))
+        return r
+
+    def anchor(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor) -> None:
+        """Step t: all partition states, their weights, and the cached composition of the far ones."""
+        self._timed("attn_anchor", _native.partition_attn, q, k, v, self.ranges, self.scale,
+                    out=self.state_out, lse=self.state_lse)
+        self._timed("contrib_anchor", self._contribution, self.state_lse, self.anchor_weights, self.anchor_scores)
+        self._timed("merge_cached", _native.merge, [self.state_out[i] for i in self.far],
+                    [self.state_lse[i] for i in self.far], out=self.cached_out, lse=self.cached_lse)
+
+    def step(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+        """Step t+1: fresh near states composed with the cached state; returns (OUT, LSE)."""
+        nf = len(self.near)
+        self._timed("attn_fresh", _native.partition_attn, q, k, v, [self.ranges[i] for i in self.near], self.scale,
+                    out=self.step_out[:nf], lse=self.step_lse[:nf])
+        self._timed("merge_step", _native.merge, [self.step_out[j] for j in range(nf + 1)],
+                    [self.step_lse[j] for j in range(nf + 1)], out=self.result_out, lse=self.result_lse)
+        self._timed("contrib_step", self._contribution, self.step_lse, self.step_weights, self.step_scores)
+        return self.result_out, self.result_lse
+
+    def _contribution(self, lse: torch.Tensor, weights: torch.Tensor, scores: torch.Tensor) -> None:
+        P = lse.shape[0]
+        _native.check(_native.lib().as_partition_contribution(
+            lse.data_ptr(), P, self.rows, self.rows_per_group, weights.data_ptr(), scores.data_ptr(),
+            self.workspace.data_ptr(), self.workspace.numel(), _native._stream(lse)))
+
+    def algorithmic_flops(self, D: int, Sq: int, B: int, H: int) -> Tuple[int, int]:
+        """FLOP of the partition-attention launches (QK^T + PV) at the anchor and at a reuse step."""
+        per_key = 4 * B * H * Sq * D
+        full = sum(e - s for s, e in self.ranges) * per_key
+        fresh = sum(self.ranges[i][1] - self.ranges[i][0] for i in self.near) * per_key
+        return full, fresh

@@ -1,0 +1,164 @@
+"""C ABI checks that need no GPU: the library loads, exports every declared entry
+point, and rejects invalid arguments on the host with the documented status and
+a message, before any HIP call (no compute calls are made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sequence_dit_amd import _native as N
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "as_attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(N.LIB_PATH), reason="libas_attn.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(as_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(N.EXPORTS), names
+    L = N.lib()
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    L = N.lib()
+    assert L.as_status_string(N.AS_OK) == b"ok"
+    assert b"invalid" in L.as_status_string(N.AS_ERR_INVALID_ARG)
+    assert b"unsupported" in L.as_status_string(N.AS_ERR_UNSUPPORTED)
+    assert b"HIP" in L.as_status_string(N.AS_ERR_HIP)
+
+
+# Fake but aligned, non-null device addresses: validation never dereferences them,
+# and every call below fails validation before reaching HIP.
+FAKE = 0x10000
+
+
+def attn(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, dtype=N.AS_BF16, B=1, H=2, Sq=16, Skv=64, D=128,
+                qs=(4096, 2048, 128), kvs=(16384, 8192, 128), ranges=[(0, 32), (32, 64)],
+                scale=0.088, out=FAKE, lse=FAKE)
+    args.update(kw)
+    rng = None
+    if args["ranges"] is not None:
+        flat = [x for r in args["ranges"] for x in r]
+        rng = (ctypes.c_int32 * max(1, len(flat)))(*flat)
+    qs = N._i64(args["qs"]) if args["qs"] is not None else None
+    kvs = N._i64(args["kvs"]) if args["kvs"] is not None else None
+    P = args.get("P", len(args["ranges"]) if args["ranges"] is not None else 1)
+    st = N.lib().as_partition_attn(args["q"], args["k"], args["v"], args["dtype"], args["B"], args["H"],
+                                   args["Sq"], args["Skv"], args["D"], qs, kvs, rng, P, args["scale"],
+                                   args["out"], args["lse"], None)
+    return st, N.lib().as_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(q=0), N.AS_ERR_INVALID_ARG, "NULL"),
+    (dict(out=0), N.AS_ERR_INVALID_ARG, "NULL"),
+    (dict(dtype=7), N.AS_ERR_INVALID_ARG, "dtype"),
+    (dict(B=-1), N.AS_ERR_INVALID_ARG, "negative"),
+    (dict(D=0), N.AS_ERR_INVALID_ARG, "D="),
+    (dict(D=96), N.AS_ERR_UNSUPPORTED, "bf16"),
+    (dict(dtype=N.AS_F32, D=130, qs=(8320, 4160, 132), kvs=(8320, 4160, 132)), N.AS_ERR_UNSUPPORTED, "f32"),
+    (dict(ranges=[(0, 65)]), N.AS_ERR_INVALID_ARG, "kv_ranges[0]"),
+    (dict(ranges=[(10, 5)]), N.AS_ERR_INVALID_ARG, "kv_ranges[0]"),
+    (dict(ranges=[(0, 4), (-1, 3)]), N.AS_ERR_INVALID_ARG, "kv_ranges[1]"),
+    (dict(ranges=None, P=2), N.AS_ERR_INVALID_ARG, "kv_ranges is NULL"),
+    (dict(ranges=[(0, 1)] * 257), N.AS_ERR_INVALID_ARG, "P=257"),
+    (dict(scale=float("nan")), N.AS_ERR_INVALID_ARG, "scale"),
+    (dict(scale=-1.0), N.AS_ERR_INVALID_ARG, "scale"),
+    (dict(q=FAKE + 8), N.AS_ERR_INVALID_ARG, "aligned"),
+    (dict(out=FAKE + 4), N.AS_ERR_INVALID_ARG, "aligned"),
+    (dict(qs=(4096, 2048, 100)), N.AS_ERR_INVALID_ARG, "multiples"),
+    (dict(kvs=(16384, 8192, 64)), N.AS_ERR_INVALID_ARG, "smaller than D"),
+    (dict(qs=None), N.AS_ERR_INVALID_ARG, "stride"),
+    (dict(B=300, H=300), N.AS_ERR_UNSUPPORTED, "65535"),
+])
+def test_partition_attn_rejects(kw, status, text):
+    st, msg = attn(**kw)
+    assert st == status, msg
+    assert text in msg
+
+
+def test_partition_attn_empty_problem_is_ok_without_gpu():
+    assert attn(Sq=0, q=0, out=0, lse=0)[0] == N.AS_OK
+    assert attn(ranges=[], P=0)[0] == N.AS_OK
+
+
+def merge_call(n=2, rows=8, D=128, outs=None, lses=None, out=FAKE, lse=FAKE):
+    outs = outs if outs is not None else [FAKE + 0x1000 * (i + 1) for i in range(n)]
+    lses = lses if lses is not None else [FAKE + 0x100000 + 0x1000 * i for i in range(n)]
+    op = (ctypes.c_void_p * max(1, len(outs)))(*outs)
+    lp = (ctypes.c_void_p * max(1, len(lses)))(*lses)
+    st = N.lib().as_merge(n, op, lp, rows, D, out, lse, None)
+    return st, N.lib().as_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(n=0), N.AS_ERR_INVALID_ARG, "n=0"),
+    (dict(n=65), N.AS_ERR_INVALID_ARG, "n=65"),
+    (dict(rows=-1), N.AS_ERR_INVALID_ARG, "negative"),
+    (dict(D=6), N.AS_ERR_INVALID_ARG, "multiple of 4"),
+    (dict(D=2048), N.AS_ERR_INVALID_ARG, "multiple of 4"),
+    (dict(out=0), N.AS_ERR_INVALID_ARG, "NULL output"),
+    (dict(out=FAKE + 8), N.AS_ERR_INVALID_ARG, "aligned"),
+    (dict(outs=[FAKE + 0x1000, 0]), N.AS_ERR_INVALID_ARG, "input 1"),
+    (dict(outs=[FAKE + 0x1000, FAKE + 0x2004]), N.AS_ERR_INVALID_ARG, "misaligned"),
+    (dict(outs=[FAKE, FAKE + 0x2000]), N.AS_ERR_INVALID_ARG, "aliases"),
+])
+def test_merge_rejects(kw, status, text):
+    st, msg = merge_call(**kw)
+    assert st == status, msg
+    assert text in msg
+
+
+def test_merge_zero_rows_ok_without_gpu():
+    assert merge_call(rows=0)[0] == N.AS_OK
+
+
+def test_contribution_workspace_size():
+    L = N.lib()
+    assert L.as_partition_contribution_workspace_size(32, 24 * 3840, 3840) == 24 * 15 * 32 * 4
+    assert L.as_partition_contribution_workspace_size(4, 10, 5) == 2 * 1 * 4 * 4
+    assert L.as_partition_contribution_workspace_size(4, 10, 3) == 0   # does not divide
+    assert L.as_partition_contribution_workspace_size(0, 10, 5) == 0
+    assert L.as_partition_contribution_workspace_size(257, 10, 5) == 0
+
+
+def contrib_call(P=4, rows=64, rpg=16, lse=FAKE, w=FAKE, s=FAKE, ws=FAKE, wsb=1 << 20):
+    st = N.lib().as_partition_contribution(lse, P, rows, rpg, w, s, ws, wsb, None)
+    return st, N.lib().as_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(P=0), N.AS_ERR_INVALID_ARG, "P=0"),
+    (dict(rows=-2), N.AS_ERR_INVALID_ARG, "negative"),
+    (dict(rpg=0), N.AS_ERR_INVALID_ARG, "rows_per_group"),
+    (dict(rpg=7), N.AS_ERR_INVALID_ARG, "multiple"),
+    (dict(lse=0), N.AS_ERR_INVALID_ARG, "lse is NULL"),
+    (dict(ws=0), N.AS_ERR_INVALID_ARG, "workspace is NULL"),
+    (dict(wsb=4), N.AS_ERR_INVALID_ARG, "smaller"),
+    (dict(ws=FAKE + 4), N.AS_ERR_INVALID_ARG, "aligned"),
+])
+def test_contribution_rejects(kw, status, text):
+    st, msg = contrib_call(**kw)
+    assert st == status, msg
+    assert text in msg
+
+
+def test_contribution_nothing_requested_ok_without_gpu():
+    assert contrib_call(w=0, s=0, ws=0)[0] == N.AS_OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="HIP device"):
+        N.partition_attn(x, x, x, [(0, 4)])

@@ -1,0 +1,296 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Tolerances (max-abs): bf16 inputs 2e-2 on OUT and 1e-3 on LSE; fp32 inputs 1e-5 on
+both; partition weights 1e-5 (fp32 arithmetic on the same LSE); empty states
+must be exactly (0, -inf). Small cases span several tiles with ragged tails and
+are checked element by element; the full-size workloads are checked on sampled
+query rows that the oracle recomputes one by one.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sequence_dit_amd import _native as N
+from sequence_dit_amd import inputs
+from sequence_dit_amd.reuse import SelectiveReuse
+
+pytestmark = pytest.mark.gpu
+
+BF16_OUT, BF16_LSE, F32_TOL = 2e-2, 1e-3, 1e-5
+DEV = "cuda:0"
+
+
+def note(msg):
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    if not os.path.exists(N.LIB_PATH):
+        pytest.fail("libas_attn.so is not built")
+    N.lib()
+
+
+def to_dev(t):
+    return t.to(DEV)
+
+
+def check_states(out, lse, o_ref, l_ref, out_tol, lse_tol, what):
+    out = out.detach().cpu().double().numpy()
+    lse = lse.detach().cpu().double().numpy()
+    empty = np.isneginf(l_ref)
+    assert np.array_equal(np.isneginf(lse), empty), f"{what}: -inf pattern differs"
+    assert np.all(out[empty] == 0), f"{what}: empty state OUT is not 0"
+    assert np.all(np.isfinite(out)), f"{what}: non-finite OUT"
+    eo = np.abs(out - o_ref).max() if out.size else 0.0
+    el = np.abs(lse[~empty] - l_ref[~empty]).max() if (~empty).any() else 0.0
+    assert eo <= out_tol, f"{what}: OUT max-abs error {eo:.3e} > {out_tol}"
+    assert el <= lse_tol, f"{what}: LSE max-abs error {el:.3e} > {lse_tol}"
+    return eo, el
+
+
+RAGGED = [(0, 200), (200, 201), (201, 201), (201, 777), (777, 1000), (100, 300), (0, 1000)]
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_bf16_small_ragged(D):
+    """Two query tiles with a ragged tail; ranges: ragged, single key, empty, tile-aligned, overlapping, full."""
+    w = inputs.small_case(7 + D, 2, 3, 300, 1000, D, RAGGED)
+    note(f"bf16 small ragged D={D} B=2 H=3 Sq=300 Skv=1000 P={len(RAGGED)}")
+    out, lse = N.partition_attn(to_dev(w.q), to_dev(w.k), to_dev(w.v), w.ranges, w.scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.partition_states(w.q, w.k, w.v, w.ranges, w.scale)
+    check_states(out, lse, o_ref, l_ref, BF16_OUT, BF16_LSE, f"bf16 D={D}")
+
+
+def test_bf16_strided_inputs_and_guarded_outputs():
+    """Non-contiguous q/k/v views and outputs followed by canaries that must stay untouched."""
+    D, B, H, Sq, Skv = 128, 1, 2, 130, 333
+    w = inputs.small_case(21, B, H, Sq, Skv, D, [(0, 333), (5, 70), (300, 333)])
+    qbig = torch.zeros(B, H, Sq + 16, D + 64, dtype=torch.bfloat16)
+    qbig[:, :, 8:8 + Sq, :D] = w.q
+    kbig = torch.zeros(B, H + 1, Skv, D + 8, dtype=torch.bfloat16)
+    vbig = torch.zeros(B, H + 1, Skv, D + 8, dtype=torch.bfloat16)
+    kbig[:, 1:, :, :D] = w.k
+    vbig[:, 1:, :, :D] = w.v
+    qd, kd, vd = to_dev(qbig)[:, :, 8:8 + Sq, :D], to_dev(kbig)[:, 1:, :, :D], to_dev(vbig)[:, 1:, :, :D]
+    P = len(w.ranges)
+    n_out, n_lse = P * B * H * Sq * D, P * B * H * Sq
+    guard = 4096
+    obuf = torch.full((n_out + guard,), 12345.0, device=DEV)
+    lbuf = torch.full((n_lse + guard,), 12345.0, device=DEV)
+    note("bf16 strided views + guarded outputs")
+    out, lse = N.partition_attn(qd, kd, vd, w.ranges, w.scale, out=obuf[:n_out].view(P, B, H, Sq, D),
+                                lse=lbuf[:n_lse].view(P, B, H, Sq))
+    torch.cuda.synchronize()
+    assert torch.all(obuf[n_out:] == 12345.0) and torch.all(lbuf[n_lse:] == 12345.0), "write past the end"
+    o_ref, l_ref = oracle.partition_states(w.q, w.k, w.v, w.ranges, w.scale)
+    check_states(out, lse, o_ref, l_ref, BF16_OUT, BF16_LSE, "bf16 strided")
+
+
+def test_bf16_large_logits_stay_finite():
+    """Scores scaled x100 (very peaked softmax): no overflow, NaN, or loss of parity."""
+    w = inputs.small_case(31, 1, 2, 64, 500, 128, [(0, 500), (0, 17), (250, 500)])
+    note("bf16 large logits")
+    out, lse = N.partition_attn(to_dev(w.q), to_dev(w.k), to_dev(w.v), w.ranges, 100 * w.scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.partition_states(w.q, w.k, w.v, w.ranges, 100 * w.scale)
+    # LSE ~ 100x larger in magnitude: allow the same relative fp32 accumulation error
+    check_states(out, lse, o_ref, l_ref, BF16_OUT, 1e-3 * 100, "bf16 x100 logits")
+
+
+def test_f32_tiny_workload_shuffled_merge_equals_full_attention():
+    """The tiny fp32 workload: states, then a merge in shuffled order, equal full attention within 1e-5."""
+    w = inputs.tiny_fp32()
+    note("f32 tiny workload")
+    out, lse = N.partition_attn(to_dev(w.q), to_dev(w.k), to_dev(w.v), w.ranges, w.scale)
+    order = w.merge_order
+    m_out, m_lse = N.merge([out[i] for i in order], [lse[i] for i in order])
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.partition_states(w.q, w.k, w.v, w.ranges, w.scale)
+    check_states(out, lse, o_ref, l_ref, F32_TOL, F32_TOL, "f32 states")
+    f_out, f_lse = oracle.full_attention(w.q, w.k, w.v, w.scale)
+    check_states(m_out, m_lse, f_out, f_lse, F32_TOL, F32_TOL, "f32 merged vs full attention")
+
+
+@pytest.mark.parametrize("D", [128, 40, 8])
+def test_f32_ragged(D):
+    w = inputs.small_case(41 + D, 1, 2, 100, 300, D, [(0, 300), (3, 4), (4, 4), (37, 251)], dtype=torch.float32)
+    note(f"f32 ragged D={D}")
+    out, lse = N.partition_attn(to_dev(w.q), to_dev(w.k), to_dev(w.v), w.ranges, w.scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.partition_states(w.q, w.k, w.v, w.ranges, w.scale)
+    check_states(out, lse, o_ref, l_ref, F32_TOL, F32_TOL, f"f32 D={D}")
+
+
+# --------------------------------------------------------------------------- #
+# merge
+# --------------------------------------------------------------------------- #
+
+def random_states(seed, n, rows, D, n_empty=0):
+    g = np.random.default_rng(seed)
+    outs = g.standard_normal((n, rows, D)).astype(np.float32)
+    lses = (g.standard_normal((n, rows)) * 4).astype(np.float32)
+    if n_empty:
+        idx = g.choice(n * rows, size=n_empty, replace=False)
+        outs.reshape(n * rows, D)[idx] = 0
+        lses.reshape(-1)[idx] = -np.inf
+    return outs, lses
+
+
+@pytest.mark.parametrize("n,rows,D", [(2, 1000, 128), (5, 777, 128), (32, 300, 128), (28, 129, 64), (64, 33, 4),
+                                      (3, 50, 1024)])
+def test_merge_matches_oracle(n, rows, D):
+    outs, lses = random_states(n * 1000 + D, n, rows, D, n_empty=rows // 3)
+    # one row where every input is empty
+    outs[:, 0] = 0
+    lses[:, 0] = -np.inf
+    note(f"merge n={n} rows={rows} D={D}")
+    od, ld = to_dev(torch.from_numpy(outs)), to_dev(torch.from_numpy(lses))
+    m_out, m_lse = N.merge(list(od), list(ld))
+    torch.cuda.synchronize()
+    r_out, r_lse = oracle.merge(outs, lses)
+    check_states(m_out, m_lse, r_out, r_lse, F32_TOL, F32_TOL, f"merge n={n}")
+
+
+def test_merge_with_empty_state_is_bitwise_identity():
+    outs, lses = random_states(5, 1, 513, 128)
+    outs[0, 3, 5] = -0.0
+    note("merge identity")
+    x_out, x_lse = to_dev(torch.from_numpy(outs[0])), to_dev(torch.from_numpy(lses[0]))
+    e_out, e_lse = torch.zeros_like(x_out), torch.full_like(x_lse, float("-inf"))
+    for ins in ([x_out, e_out], [e_out, x_out], [e_out, x_out, e_out]):
+        lins = [x_lse if t is x_out else e_lse for t in ins]
+        m_out, m_lse = N.merge(ins, lins)
+        torch.cuda.synchronize()
+        assert torch.equal(m_out.view(torch.int32), x_out.view(torch.int32)), "OUT bits changed"
+        assert torch.equal(m_lse.view(torch.int32), x_lse.view(torch.int32)), "LSE bits changed"
+    m_out, m_lse = N.merge([e_out, e_out], [e_lse, e_lse])
+    torch.cuda.synchronize()
+    assert torch.all(m_out == 0) and torch.all(torch.isneginf(m_lse))
+
+
+def test_merge_tree_equals_flat_on_gpu():
+    """Associativity and commutativity on the device: ((a,b),(c,(d,e))) equals the flat 5-way merge."""
+    outs, lses = random_states(77, 5, 400, 128)
+    od, ld = list(to_dev(torch.from_numpy(outs))), list(to_dev(torch.from_numpy(lses)))
+    note("merge tree")
+    ab = N.merge([od[1], od[0]], [ld[1], ld[0]])
+    de = N.merge([od[4], od[3]], [ld[4], ld[3]])
+    cde = N.merge([de[0], od[2]], [de[1], ld[2]])
+    t_out, t_lse = N.merge([cde[0], ab[0]], [cde[1], ab[1]])
+    f_out, f_lse = N.merge(od, ld)
+    torch.cuda.synchronize()
+    assert (t_out - f_out).abs().max().item() <= F32_TOL
+    assert (t_lse - f_lse).abs().max().item() <= F32_TOL
+
+
+# --------------------------------------------------------------------------- #
+# contribution
+# --------------------------------------------------------------------------- #
+
+@pytest.mark.parametrize("P,rows,rpg", [(32, 2 * 3840, 3840), (5, 1000, 250), (8, 777, 777), (3, 64, 1), (256, 300, 100)])
+def test_contribution_matches_oracle(P, rows, rpg):
+    g = np.random.default_rng(P * 7 + rows)
+    lse = (g.standard_normal((P, rows)) * 6).astype(np.float32)
+    lse[0, :5] = -np.inf
+    lse[:, 7] = -np.inf  # a row with every partition empty
+    note(f"contribution P={P} rows={rows} rpg={rpg}")
+    ld = to_dev(torch.from_numpy(lse))
+    w, s = N.partition_contribution(ld, rpg)
+    w2, s2 = N.partition_contribution(ld, rpg)
+    torch.cuda.synchronize()
+    w_ref, s_ref = oracle.contribution(lse, rpg)
+    assert np.abs(w.cpu().double().numpy() - w_ref).max() <= F32_TOL
+    assert np.abs(s.cpu().double().numpy() - s_ref).max() <= F32_TOL
+    assert torch.equal(s, s2) and torch.equal(w, w2), "not deterministic"
+
+
+# --------------------------------------------------------------------------- #
+# Full-size workloads, sampled rows
+# --------------------------------------------------------------------------- #
+
+def sampled_reference(w, q, k, v, heads, rows_sel, ranges):
+    qs = q[:, heads][:, :, rows_sel]
+    return oracle.partition_states(qs, k[:, heads], v[:, heads], ranges, w.scale)
+
+
+def sample_rows(Sq, n=24, seed=0):
+    g = np.random.default_rng(seed)
+    picks = set(g.choice(Sq, size=min(n, Sq), replace=False).tolist()) | {0, Sq - 1, min(255, Sq - 1), min(256, Sq - 1)}
+    return sorted(picks)
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_full_size_image_and_video(cfg):
+    w = inputs.make(cfg)
+    note(f"full size workload: {w.name}")
+    q, k, v = to_dev(w.q), to_dev(w.k), to_dev(w.v)
+    out, lse = N.partition_attn(q, k, v, w.ranges, w.scale)
+    m_out, m_lse = N.merge(list(out), list(lse))
+    torch.cuda.synchronize()
+    heads = [0, w.H // 2, w.H - 1]
+    rs = sample_rows(w.Sq, seed=cfg)
+    o_ref, l_ref = sampled_reference(w, w.q, w.k, w.v, heads, rs, w.ranges)
+    got_o = out[:, :, heads][:, :, :, rs]
+    got_l = lse[:, :, heads][:, :, :, rs]
+    check_states(got_o, got_l, o_ref, l_ref, BF16_OUT, BF16_LSE, f"config {cfg} states")
+    f_o, f_l = oracle.merge(o_ref, l_ref)
+    check_states(m_out[:, heads][:, :, rs], m_lse[:, heads][:, :, rs], f_o, f_l, BF16_OUT, BF16_LSE,
+                 f"config {cfg} merged")
+
+
+@pytest.fixture(scope="module")
+def reuse_workload():
+    return inputs.selective_reuse()
+
+
+def test_full_size_long_video_and_selective_reuse(reuse_workload):
+    """Long-video states (all 32 partitions) and the selective-reuse step at full size, on sampled rows."""
+    w = reuse_workload
+    note(f"full size workload: {w.name}")
+    B, H, Sq, D = w.B, w.H, w.Sq, w.D
+    runner = SelectiveReuse(B, H, Sq, D, w.ranges, w.near, DEV, w.scale)
+    q, k, v = to_dev(w.q), to_dev(w.k), to_dev(w.v)
+    runner.anchor(q, k, v)
+    del q, k, v
+    q1, k1, v1 = to_dev(w.q1), to_dev(w.k1), to_dev(w.v1)
+    r_out, r_lse = runner.step(q1, k1, v1)
+    # full attention at t+1 on the GPU for the reported MSE
+    full_out, full_lse = N.partition_attn(q1, k1, v1, w.ranges, w.scale)
+    f_out, f_lse = N.merge(list(full_out), list(full_lse))
+    torch.cuda.synchronize()
+
+    heads = [0, 11, 23]
+    rs = sample_rows(Sq, n=16, seed=5)
+    o_t, l_t = sampled_reference(w, w.q, w.k, w.v, heads, rs, w.ranges)
+    o_t1, l_t1 = sampled_reference(w, w.q1, w.k1, w.v1, heads, rs, w.ranges)
+    check_states(runner.state_out[:, :, heads][:, :, :, rs], runner.state_lse[:, :, heads][:, :, :, rs],
+                 o_t, l_t, BF16_OUT, BF16_LSE, "long video states (step t)")
+    ref_out, ref_lse, c_out, c_lse = oracle.selective_reuse(o_t, l_t, o_t1, l_t1, w.near)
+    check_states(runner.cached_out[:, heads][:, :, rs], runner.cached_lse[:, heads][:, :, rs], c_out, c_lse,
+                 BF16_OUT, BF16_LSE, "cached composed state")
+    check_states(r_out[:, heads][:, :, rs], r_lse[:, heads][:, :, rs], ref_out, ref_lse, BF16_OUT, BF16_LSE,
+                 "selective reuse result")
+    full_ref = oracle.merge(o_t1, l_t1)
+    check_states(f_out[:, heads][:, :, rs], f_lse[:, heads][:, :, rs], full_ref[0], full_ref[1], BF16_OUT,
+                 BF16_LSE, "full attention t+1")
+    # weights at the anchor and at the reuse step against the oracle on the GPU's LSE
+    w_ref, s_ref = oracle.contribution(runner.state_lse.reshape(w.P, -1).cpu().numpy(), Sq)
+    assert np.abs(runner.anchor_weights.cpu().double().numpy() - w_ref).max() <= F32_TOL
+    assert np.abs(runner.anchor_scores.cpu().double().numpy() - s_ref).max() <= F32_TOL
+    w5, s5 = oracle.contribution(runner.step_lse.reshape(len(w.near) + 1, -1).cpu().numpy(), Sq)
+    assert np.abs(runner.step_scores.cpu().double().numpy() - s5).max() <= F32_TOL
+    # reuse error against full attention: reported; the near partitions hold most of the mass
+    mse = torch.mean((r_out - f_out) ** 2).item()
+    mean_w = runner.anchor_scores.mean(0).cpu().numpy()
+    note(f"selective reuse: MSE vs full attention {mse:.3e}; near weight {mean_w[w.near].sum():.3f}")
+    assert mean_w[w.near].sum() > 0.5
+    assert mse < 1e-2
