@@ -282,7 +282,9 @@ void attn_bf16_kernel(const AttnArgs a) {
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
       const float nm = -m[qb];
-      float acc = l[qb];
+      // the row sum uses the fp32 probabilities: summing their bf16 roundings
+      // would put the bf16 unit roundoff (2^-8) straight into LSE
+      float acc0 = l[qb], acc1 = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -292,14 +294,14 @@ void attn_bf16_kernel(const AttnArgs a) {
           for (int e = 0; e < 8; e += 2) {
             const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][8 * c + e], c2, nm));
             const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][8 * c + e + 1], c2, nm));
-            const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
-            acc = __builtin_amdgcn_fdot2_f32_bf16(pp, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, acc, false);
-            p[e] = pp[0];
-            p[e + 1] = pp[1];
+            acc0 += p0;
+            acc1 += p1;
+            p[e] = (__bf16)p0;
+            p[e + 1] = (__bf16)p1;
           }
           pf[qb][kb][c] = p;
         }
-      l[qb] = acc;
+      l[qb] = acc0 + acc1;
     }
 
     // ---- O^T += V^T P^T
