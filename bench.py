@@ -107,6 +107,9 @@ def main():
     ap.add_argument("--config", type=int, default=5, choices=[2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run one plain device copy (y = x * 1, fp32) reading and writing this many MiB, "
+                         "outside the timed region, to calibrate HBM byte counters")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -150,6 +153,12 @@ def main():
             runner._timed("merge_all", N.merge, [runner.state_out[i] for i in all_idx],
                           [runner.state_lse[i] for i in all_idx], out=merge_out, lse=merge_lse)
 
+    if args.copy_mib:
+        x = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        torch.mul(x, 1.0, out=y)
+        torch.cuda.synchronize()
+        del x, y
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):

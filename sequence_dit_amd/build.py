@@ -23,6 +23,11 @@ ARCH = "gfx950"
 
 SOURCES = ["api.hip", "partition_attn.hip", "merge.hip", "contribution.hip"]
 
+# Per-source flags. The attention kernels never see NaN (finite inputs, -inf only
+# as a max/exp operand), so NaN-honouring max and IEEE-mode operand
+# canonicalisation are switched off there: fmaxf becomes a single v_max/v_max3.
+SOURCE_FLAGS = {"partition_attn.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+
 # Packed fp32 VALU instructions are kept out of the device code on purpose: hipcc
 # only emits them from ordinary float code, and the kernels do not need them.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -58,7 +63,8 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([cc, *COMMON_FLAGS, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([cc, *COMMON_FLAGS, *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
+                     "-o", obj])
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as pool:
         list(pool.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB_PATH + ".tmp"

@@ -79,19 +79,245 @@ __device__ __forceinline__ float wave_sum_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// LDS-only workgroup barrier: waits for this wave's LDS operations, not for its
+// outstanding global loads (those are consumed phases later).
+// The scheduling fences keep the compiler from moving ALU work of one phase across
+// the barrier into the next phase.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Instruction classes for __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
+// LDS layout of one workgroup (bytes). Rows are padded by 16 bytes instead of
+// XOR-swizzled, so every operand address is a per-lane base plus a compile-time
+// immediate. K tiles are [key][d]; V tiles are transposed, [d][key], with the keys
+// of a row permuted so that the 8 keys one lane feeds to an MFMA are contiguous.
+template <int D>
+struct Lds {
+  static constexpr int KP = D * 2 + 16;        // K row pitch
+  static constexpr int KTILE = kBK * KP;
+  static constexpr int VP = kBK * 2 + 16;      // V^T row pitch
+  static constexpr int VTILE = D * VP;
+  static constexpr int V0 = 2 * KTILE;         // two K slots, then two V slots
+  static constexpr int BYTES = 2 * KTILE + 2 * VTILE;
+};
+
+// Position (bytes) of 4-key group g (keys 4g..4g+3 of a 64-key tile) in a V^T row.
+// The MFMA operand of lane half h for (key block kb, step c) is the key groups
+// 8kb+4c+h and 8kb+4c+h+2, stored side by side as 16-byte chunk 4kb+2c+h.
+__device__ __forceinline__ constexpr int vt_group_pos(int g) {
+  return 16 * (((g >> 2) << 1) | (g & 1)) + 8 * ((g >> 1) & 1);
+}
+
+// Per-wave state of the bf16 kernel; one wave owns 32 query rows.
+template <int D>
+struct Wave {
+  static constexpr int NDS = D / 16;   // MFMA k-steps of S^T = K Q^T
+  static constexpr int NDB = D / 32;   // 32-wide d blocks of O^T
+  bf16x8 qf[NDS];        // Q (B operand of S^T): Q[row l32][d = 16ds + 8half .. +7]
+  f32x16 s[2];           // S^T of the current tile: [kb], reg r <-> key 32kb + 8(r/4) + 4half + r%4
+  bf16x8 pf[2][2];       // P of the previous tile, B operand of O^T: [kb][c]
+  f32x16 o[NDB];         // O^T: [db], reg r <-> d = 32db + 8(r/4) + 4half + r%4
+  float m, l;            // running max (log2 domain, scaled) and row sum
+  int k_rd, v_rd;        // LDS read bases of this lane
+
+  // MFMA phase of tile t: S_t = K_t Q^T from K slot KS (if DO_S) and
+  // O^T += V_{t-1}^T P_{t-1}^T from V slot VS (if DO_PV). Operand reads run six
+  // ahead of the MFMAs that consume them.
+  template <int KS, int VS, bool DO_S, bool DO_PV>
+  __device__ __forceinline__ void mfma_phase(const char* smem) {
+    using L = Lds<D>;
+    constexpr int NS = DO_S ? 2 * NDS : 0;
+    constexpr int NPV = DO_PV ? 4 * NDB : 0;
+    constexpr int N = NS + NPV;
+    constexpr int NMAX = NS > NPV ? NS : NPV;
+    bf16x8 kf[2 * NDS > 0 ? 2 * NDS : 1];
+    bf16x8 vf[4 * NDB];
+    if (DO_S) {
+      s[0] = f32x16{};
+      s[1] = f32x16{};
+    }
+#pragma unroll
+    for (int i = 0; i < NMAX; ++i) {
+      if (i < NS) {
+        const int ds = i >> 1, kb = i & 1;
+        kf[i] = *reinterpret_cast<const bf16x8*>(smem + k_rd + KS * L::KTILE + kb * 32 * L::KP + ds * 32);
+      }
+      if (i < NPV) {
+        const int kbc = i / NDB, db = i % NDB;     // kbc = 2kb + c
+        vf[i] = *reinterpret_cast<const bf16x8*>(smem + v_rd + VS * L::VTILE + db * 32 * L::VP + 32 * kbc);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NMAX; ++i) {
+      if (i < NS) {
+        const int ds = i >> 1, kb = i & 1;
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[ds], s[kb], 0, 0, 0);
+      }
+      if (i < NPV) {
+        const int kbc = i / NDB, db = i % NDB;
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[kbc >> 1][kbc & 1], o[db], 0, 0, 0);
+      }
+    }
+    constexpr int LA = N < 6 ? N : 6;
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, LA, 0);
+#pragma unroll
+    for (int i = 0; i < N - LA; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, LA, 0);
+  }
+
+  // Softmax phase of tile t: online softmax of S_t (exp2 domain, lazy rescale) -> P_t.
+  // valid = keys of the tile inside the partition.
+  __device__ __forceinline__ void softmax_phase(int valid, float c2, int half) {
+    if (valid < kBK) softmax<true>(valid, c2, half);
+    else softmax<false>(valid, c2, half);
+  }
+
+  template <bool MASK>
+  __device__ __forceinline__ void softmax(int valid, float c2, int half) {
+    if (MASK) {  // keys past the end of the partition
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (key >= valid) s[kb][r] = -INFINITY;
+        }
+    }
+    float x = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) x = fmaxf(x, fmaxf(s[0][r], s[1][r]));
+    const float mx = wave_max_halves(x) * c2;
+    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleThreshold) != 0) {
+      const float mn = fmaxf(m, mx);
+      const float f = __builtin_amdgcn_exp2f(m - mn);
+      m = mn;
+      l *= f;
+      // in-place multiplies: keeps the accumulators in their registers across the branch
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) asm volatile("v_mul_f32 %0, %0, %1" : "+v"(o[db][r]) : "v"(f));
+    }
+    const float nm = -m;
+    // the row sum uses the fp32 probabilities: summing their bf16 roundings
+    // would put the bf16 unit roundoff (2^-8) straight into LSE
+    float acc0 = l, acc1 = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        bf16x8 p;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * c + e], c2, nm));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * c + e + 1], c2, nm));
+          acc0 += p0;
+          acc1 += p1;
+          p[e] = (__bf16)p0;
+          p[e + 1] = (__bf16)p1;
+        }
+        pf[kb][c] = p;
+      }
+    l = acc0 + acc1;
+  }
+};
+
+// Tile staging. Group 1 (waves 4-7) owns K: 16-byte chunks, a row per 16 lanes.
+// Group 0 (waves 0-3) owns V: a unit is 4 keys x 8 d, transposed in registers and
+// written as 8-byte key groups of 8 V^T rows; the 16 lanes of a write pass cover
+// the 16 key groups of one row.
+template <int D>
+struct Stager {
+  static constexpr int KCH = D / 8;                 // 16-byte chunks per K row
+  static constexpr int GT = kThreads / 2;           // threads per group
+  static constexpr int KLOADS = kBK * KCH / GT;     // K chunks per thread
+  static constexpr int KROWS = GT / KCH;            // K rows per load round
+  static constexpr int VUNITS = (kBK / 4) * KCH;    // V units per tile
+  static constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw 32-bit buffer, no swizzle
+  u32x4 r[4];
+  const __bf16* src;     // K or V rows of this (b, h) starting at the partition
+  int64_t row_stride;    // elements
+  int stride_bytes;
+  int n;                 // keys in the partition
+  int voff[4];           // byte offsets of this thread's loads within a tile
+  int w_off;             // LDS write base of this thread
+  bool on;
+
+  // Buffer resource covering exactly the valid rows of tile `tile`: loads past the
+  // partition's end are range-checked by the hardware and return zeros, without a
+  // branch or a clamp per lane. A tile past the end gets an empty range.
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(int tile) const {
+    const int rows = n - tile * kBK;
+    const int bytes = rows > 0 ? (min(rows, kBK) - 1) * stride_bytes + D * 2 : 0;
+    const uint64_t base = reinterpret_cast<uint64_t>(src + (int64_t)(rows > 0 ? tile * kBK : 0) * row_stride);
+    // all of it is wave-uniform; readfirstlane keeps the descriptor in SGPRs
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(lo | (hi << 32)), (short)0,
+                                             __builtin_amdgcn_readfirstlane(bytes), kRsrcWord3);
+  }
+  __device__ __forceinline__ void load_k(int tile) {
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(tile);
+#pragma unroll
+    for (int j = 0; j < KLOADS; ++j) r[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff[j], 0, 0);
+  }
+  template <int SLOT>
+  __device__ __forceinline__ void store_k(char* smem) {
+    using L = Lds<D>;
+#pragma unroll
+    for (int j = 0; j < KLOADS; ++j)
+      *reinterpret_cast<u32x4*>(smem + w_off + SLOT * L::KTILE + j * KROWS * L::KP) = r[j];
+  }
+  __device__ __forceinline__ void load_v(int tile) {
+    if (!on) return;
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(tile);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff[j], 0, 0);
+  }
+  template <int SLOT>
+  __device__ __forceinline__ void store_v(char* smem) {
+    using L = Lds<D>;
+    if (!on) return;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const unsigned v0 = r[0][w], v1 = r[1][w], v2 = r[2][w], v3 = r[3][w];
+      // d = 8c + 2w takes the low halves, d = 8c + 2w + 1 the high halves
+      const u32x2 lo = {__builtin_amdgcn_perm(v1, v0, 0x05040100u), __builtin_amdgcn_perm(v3, v2, 0x05040100u)};
+      const u32x2 hi = {__builtin_amdgcn_perm(v1, v0, 0x07060302u), __builtin_amdgcn_perm(v3, v2, 0x07060302u)};
+      *reinterpret_cast<u32x2*>(smem + w_off + SLOT * L::VTILE + (2 * w) * L::VP) = lo;
+      *reinterpret_cast<u32x2*>(smem + w_off + SLOT * L::VTILE + (2 * w + 1) * L::VP) = hi;
+    }
+  }
+};
+
+// Schedule ("ping-pong"): the 8 waves form two groups of 4, one wave of each group
+// per SIMD. Every wave alternates an MFMA phase X_t (S_t = K_t Q^T and
+// O += V_{t-1} P_{t-1}^T) with a VALU phase Y_t (softmax of S_t -> P_t, plus tile
+// staging), separated by workgroup barriers. Group 1 runs one phase behind group 0,
+// so on each SIMD one wave is in its MFMA phase while the other is in its VALU
+// phase (a wave does not overlap its own VALU work with its own MFMAs). Group 1
+// stages K (tile t+2 during Y_t), group 0 stages V (tile t during Y_t); two LDS
+// slots per operand suffice for this offset: a slot is rewritten only after both
+// groups' last read of its previous tile.
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_kernel(const AttnArgs a) {
-  constexpr int NDS = D / 16;        // MFMA k-steps of S^T = K Q^T
-  constexpr int NDB = D / 32;        // 32-wide d blocks of O^T
-  constexpr int KCH = D / 8;         // 16-byte chunks per K row
-  constexpr int KTILE = kBK * D * 2; // bytes of one K tile
-  constexpr int VTILE = D * kBK * 2; // bytes of one transposed V tile
-  constexpr int STAGE = KTILE + VTILE;
-  constexpr int KLOADS = kBK * KCH / kThreads;   // 16-byte K chunks per thread
-  constexpr int VUNITS = (kBK / 4) * KCH;        // 4 keys x 8 d units of V
-  static_assert(KLOADS >= 1 && VUNITS <= kThreads, "tile shape");
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  using L = Lds<D>;
+  using W = Wave<D>;
+  using St = Stager<D>;
+  static_assert(kQB == 1 && St::KLOADS >= 1 && St::KLOADS <= 4 && St::VUNITS <= St::GT, "tile shape");
+  __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
 
   const int total = a.n_qtiles * a.B * a.H * a.P;
   const int lid = xcd_remap(blockIdx.x, total);
@@ -104,6 +330,9 @@ void attn_bf16_kernel(const AttnArgs a) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, half = lane >> 5;
+  // wave-uniform; readfirstlane lets the compiler keep group-dependent values in SGPRs
+  const int grp = __builtin_amdgcn_readfirstlane(tid >> 8);
+  const int gtid = tid & (St::GT - 1);
 
   const int ks = a.ranges[2 * part], ke = a.ranges[2 * part + 1];
   const int n = ke - ks;
@@ -124,225 +353,143 @@ void attn_bf16_kernel(const AttnArgs a) {
     return;
   }
 
-  // ---- Q fragments (B operand of S^T): lane holds Q[row = l32][d = ds*16 + 8*half .. +7]
+  W w;
   const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + b * a.q_sb + hh * a.q_sh;
-  bf16x8 qf[kQB][NDS];
+  const int qrow = q0 + wave * kRowsPerWave + l32;
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    const int q = q0 + wave * kRowsPerWave + qb * 32 + l32;
+  for (int ds = 0; ds < W::NDS; ++ds) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(qp + (int64_t)min(qrow, a.Sq - 1) * a.q_ss + ds * 16 + 8 * half);
+    w.qf[ds] = __builtin_bit_cast(bf16x8, qrow < a.Sq ? x : u32x4{0u, 0u, 0u, 0u});
+  }
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (q < a.Sq) x = *reinterpret_cast<const u32x4*>(qp + (int64_t)q * a.q_ss + ds * 16 + 8 * half);
-      qf[qb][ds] = __builtin_bit_cast(bf16x8, x);
-    }
+  for (int db = 0; db < W::NDB; ++db) w.o[db] = f32x16{};
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) w.pf[kb][c] = bf16x8{};
+  w.m = -INFINITY;
+  w.l = 0.f;
+  w.k_rd = l32 * L::KP + 16 * half;
+  w.v_rd = L::V0 + l32 * L::VP + 16 * half;
+  const float c2 = a.scale_log2;
+  const int T = (n + kBK - 1) / kBK;
+
+  St st;
+  st.n = n;
+  st.row_stride = a.k_ss;
+  st.stride_bytes = (int)(a.k_ss * 2);
+  const int64_t kv_off = b * a.k_sb + hh * a.k_sh + (int64_t)ks * a.k_ss;
+  if (grp == 1) {
+    st.src = reinterpret_cast<const __bf16*>(a.k) + kv_off;
+    const int row = gtid / St::KCH, ch = gtid % St::KCH;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) st.voff[j] = (row + j * St::KROWS) * st.stride_bytes + ch * 16;
+    st.w_off = row * L::KP + ch * 16;
+    st.on = true;
+  } else {
+    st.src = reinterpret_cast<const __bf16*>(a.v) + kv_off;
+    const int va = gtid & 15, vc = gtid >> 4;   // 4-key group, 8-wide d chunk
+#pragma unroll
+    for (int j = 0; j < 4; ++j) st.voff[j] = (4 * va + j) * st.stride_bytes + vc * 16;
+    st.w_off = L::V0 + (8 * vc) * L::VP + vt_group_pos(va);
+    st.on = gtid < St::VUNITS;
   }
 
-  const __bf16* kp = reinterpret_cast<const __bf16*>(a.k) + b * a.k_sb + hh * a.k_sh + (int64_t)ks * a.k_ss;
-  const __bf16* vp = reinterpret_cast<const __bf16*>(a.v) + b * a.k_sb + hh * a.k_sh + (int64_t)ks * a.k_ss;
-  const int64_t kss = a.k_ss;
-  const int ntiles = (n + kBK - 1) / kBK;
-
-  // ---- staging registers and their LDS destinations
-  u32x4 kreg[KLOADS];
-  u32x4 vreg[4];
-  const int vu_c = tid % KCH;       // V unit: 8-wide d chunk
-  const int vu_a = tid / KCH;       // V unit: 4-key group
-  const bool vu_on = tid < VUNITS;
-
-  auto gload = [&](int tile) {
-    const int key0 = tile * kBK;
-#pragma unroll
-    for (int j = 0; j < KLOADS; ++j) {
-      const int c = tid + j * kThreads;
-      const int row = c / KCH, ch = c % KCH;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (key0 + row < n) x = *reinterpret_cast<const u32x4*>(kp + (int64_t)(key0 + row) * kss + ch * 8);
-      kreg[j] = x;
+  // Both groups pass 2T + 3 barriers: group 1's extra leading phase (staging
+  // K tile 1) is matched by group 0's trailing empty phase.
+  if (grp == 1) {
+    st.load_k(0);
+    st.template store_k<0>(smem);
+    st.load_k(1);
+    lds_barrier();                                   // K tile 0 visible
+    if (T > 1) st.template store_k<1>(smem);         // phase Y_{-1}
+    st.load_k(2);
+    lds_barrier();
+    w.template mfma_phase<0, 0, true, false>(smem);  // X_0
+    lds_barrier();
+    w.softmax_phase(n, c2, half);                    // Y_0
+    if (T > 2) st.template store_k<0>(smem);
+    st.load_k(3);
+    lds_barrier();
+    int t = 1;
+    for (; t + 1 < T; t += 2) {
+      w.template mfma_phase<1, 0, true, true>(smem);     // X_t, t odd
+      lds_barrier();
+      w.softmax_phase(n - t * kBK, c2, half);
+      if (t + 2 < T) st.template store_k<1>(smem);
+      st.load_k(t + 3);
+      lds_barrier();
+      w.template mfma_phase<0, 1, true, true>(smem);     // X_{t+1}, even
+      lds_barrier();
+      w.softmax_phase(n - (t + 1) * kBK, c2, half);
+      if (t + 3 < T) st.template store_k<0>(smem);
+      st.load_k(t + 4);
+      lds_barrier();
     }
-    if (vu_on) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = 4 * vu_a + j;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (key0 + row < n) x = *reinterpret_cast<const u32x4*>(vp + (int64_t)(key0 + row) * kss + vu_c * 8);
-        vreg[j] = x;
-      }
+    if (t < T) {  // t odd, last tile
+      w.template mfma_phase<1, 0, true, true>(smem);
+      lds_barrier();
+      w.softmax_phase(n - t * kBK, c2, half);
+      lds_barrier();
+      w.template mfma_phase<0, 1, false, true>(smem);    // X_T, V slot (T-1)&1 = 1
+    } else {      // T even (or 1): V slot (T-1)&1
+      if (T & 1) w.template mfma_phase<0, 0, false, true>(smem);
+      else w.template mfma_phase<0, 1, false, true>(smem);
     }
-  };
-
-  auto swrite = [&](int stage) {
-    char* kt = smem + stage * STAGE;
-#pragma unroll
-    for (int j = 0; j < KLOADS; ++j) {
-      const int c = tid + j * kThreads;
-      const int row = c / KCH, ch = c % KCH;
-      *reinterpret_cast<u32x4*>(kt + row * (D * 2) + ((ch ^ (row & (KCH - 1))) * 16)) = kreg[j];
+    lds_barrier();
+  } else {
+    st.load_v(0);
+    lds_barrier();
+    w.template mfma_phase<0, 0, true, false>(smem);  // X_0
+    lds_barrier();
+    w.softmax_phase(n, c2, half);                    // Y_0
+    st.template store_v<0>(smem);
+    st.load_v(1);
+    lds_barrier();
+    int t = 1;
+    for (; t + 1 < T; t += 2) {
+      w.template mfma_phase<1, 0, true, true>(smem);
+      lds_barrier();
+      w.softmax_phase(n - t * kBK, c2, half);
+      st.template store_v<1>(smem);
+      st.load_v(t + 1);
+      lds_barrier();
+      w.template mfma_phase<0, 1, true, true>(smem);
+      lds_barrier();
+      w.softmax_phase(n - (t + 1) * kBK, c2, half);
+      st.template store_v<0>(smem);
+      st.load_v(t + 2);
+      lds_barrier();
     }
-    if (vu_on) {
-      char* vt = kt + KTILE;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const unsigned v0 = vreg[0][w], v1 = vreg[1][w], v2 = vreg[2][w], v3 = vreg[3][w];
-        // d = 8c + 2w takes the low halves, d = 8c + 2w + 1 the high halves
-        const u32x2 lo = {__builtin_amdgcn_perm(v1, v0, 0x05040100u), __builtin_amdgcn_perm(v3, v2, 0x05040100u)};
-        const u32x2 hi = {__builtin_amdgcn_perm(v1, v0, 0x07060302u), __builtin_amdgcn_perm(v3, v2, 0x07060302u)};
-        const int d0 = 8 * vu_c + 2 * w, d1 = d0 + 1;
-        *reinterpret_cast<u32x2*>(vt + d0 * (kBK * 2) + ((vu_a ^ vt_swz(d0)) * 8)) = lo;
-        *reinterpret_cast<u32x2*>(vt + d1 * (kBK * 2) + ((vu_a ^ vt_swz(d1)) * 8)) = hi;
-      }
+    if (t < T) {
+      w.template mfma_phase<1, 0, true, true>(smem);
+      lds_barrier();
+      w.softmax_phase(n - t * kBK, c2, half);
+      st.template store_v<1>(smem);
+      lds_barrier();
+      w.template mfma_phase<0, 1, false, true>(smem);
+    } else {
+      if (T & 1) w.template mfma_phase<0, 0, false, true>(smem);
+      else w.template mfma_phase<0, 1, false, true>(smem);
     }
-  };
-
-  // per-lane LDS read offsets
-  const int krow_swz = l32 & (KCH - 1);
-  int vt_off[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) vt_off[db] = (db * 32 + l32) * (kBK * 2);
-  int vt_sw[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) vt_sw[db] = vt_swz(db * 32 + l32);
-
-  f32x16 o[NDB][kQB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) o[db][qb] = f32x16{};
-  float m[kQB], l[kQB];
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) { m[qb] = -INFINITY; l[qb] = 0.f; }
-  const float c2 = a.scale_log2;
-
-  gload(0);
-  swrite(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int stage = t & 1;
-    if (t + 1 < ntiles) gload(t + 1);
-    const char* kt = smem + stage * STAGE;
-    const char* vt = kt + KTILE;
-
-    // ---- S^T = K Q^T : s[kb][qb], lane (l32, half), reg r <-> key kb*32 + 8(r/4) + 4half + r%4, query l32
-    f32x16 s[2][kQB];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) s[kb][qb] = f32x16{};
-#pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-        const int row = kb * 32 + l32;
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt + row * (D * 2) + (((2 * ds + half) ^ krow_swz) * 16));
-#pragma unroll
-        for (int qb = 0; qb < kQB; ++qb)
-          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ds], s[kb][qb], 0, 0, 0);
-      }
-    }
-
-    // ---- mask keys past the end of the partition (last tile only)
-    const int valid = n - t * kBK;
-    if (valid < kBK) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (key >= valid) {
-#pragma unroll
-            for (int qb = 0; qb < kQB; ++qb) s[kb][qb][r] = -INFINITY;
-          }
-        }
-    }
-
-    // ---- online softmax (exp2 domain, lazy rescale)
-    float mx[kQB];
-    bool need = false;
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      float x = s[0][qb][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) x = fmaxf(x, s[0][qb][r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x = fmaxf(x, s[1][qb][r]);
-      mx[qb] = wave_max_halves(x) * c2;
-      need |= mx[qb] > m[qb] + kRescaleThreshold;
-    }
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) {
-        const float mn = fmaxf(m[qb], mx[qb]);
-        const float f = __builtin_amdgcn_exp2f(m[qb] - mn);
-        m[qb] = mn;
-        l[qb] *= f;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) o[db][qb] *= f;
-      }
-    }
-    bf16x8 pf[kQB][2][2];   // [qb][kb][c]: B operand of O^T for keys kb*32 + 16c + ...
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      const float nm = -m[qb];
-      // the row sum uses the fp32 probabilities: summing their bf16 roundings
-      // would put the bf16 unit roundoff (2^-8) straight into LSE
-      float acc0 = l[qb], acc1 = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          bf16x8 p;
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][8 * c + e], c2, nm));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][8 * c + e + 1], c2, nm));
-            acc0 += p0;
-            acc1 += p1;
-            p[e] = (__bf16)p0;
-            p[e + 1] = (__bf16)p1;
-          }
-          pf[qb][kb][c] = p;
-        }
-      l[qb] = acc0 + acc1;
-    }
-
-    // ---- O^T += V^T P^T
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int g = 8 * kb + 4 * c + half;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vt + vt_off[db] + ((g ^ vt_sw[db]) * 8));
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vt + vt_off[db] + (((g + 2) ^ vt_sw[db]) * 8));
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-#pragma unroll
-          for (int qb = 0; qb < kQB; ++qb)
-            o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][kb][c], o[db][qb], 0, 0, 0);
-        }
-      }
-
-    if (t + 1 < ntiles) swrite(stage ^ 1);
-    __syncthreads();
+    lds_barrier();
+    lds_barrier();   // group 1's trailing X_T phase
   }
 
   // ---- epilogue: OUT = O / l, LSE = (m + log2 l) ln 2
+  const float lt = wave_sum_halves(w.l);
+  const float inv = 1.0f / lt;
+  if (qrow < a.Sq) {
+    float* orow = out + (int64_t)qrow * D;
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    const float lt = wave_sum_halves(l[qb]);
-    const float inv = 1.0f / lt;
-    const int q = q0 + wave * kRowsPerWave + qb * 32 + l32;
-    if (q < a.Sq) {
-      float* orow = out + (int64_t)q * D;
+    for (int db = 0; db < W::NDB; ++db)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f32x4 val = {o[db][qb][4 * j] * inv, o[db][qb][4 * j + 1] * inv,
-                             o[db][qb][4 * j + 2] * inv, o[db][qb][4 * j + 3] * inv};
-          *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * j + 4 * half) = val;
-        }
-      if (half == 0) lse[q] = (m[qb] + __log2f(lt)) * 0.69314718055994530942f;
-    }
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 val = {w.o[db][4 * j] * inv, w.o[db][4 * j + 1] * inv, w.o[db][4 * j + 2] * inv,
+                           w.o[db][4 * j + 3] * inv};
+        *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * j + 4 * half) = val;
+      }
+    if (half == 0) lse[qrow] = (w.m + __log2f(lt)) * 0.69314718055994530942f;
   }
 }
 
