@@ -27,7 +27,7 @@ sys.path.insert(0, ROOT)
 METRIC = "partition-attn TFLOP/s (% bf16 MFMA peak) + as_merge GB/s (% HBM peak), 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "partition_attn_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "partition_attn_traffic.txt")
 ATTN_SOURCE = os.path.join(ROOT, "sequence_dit_amd", "csrc", "partition_attn.hip")
 
 
@@ -41,15 +41,23 @@ def source_digest(path=ATTN_SOURCE):
 
 
 def measured_traffic():
-    """HBM bytes per attention launch from the committed PMC capture, if it matches the current kernel source."""
+    """HBM bytes per attention launch from the committed counter summary (``key: value`` lines),
+    or None when that summary was taken on a different kernel source."""
+    t = {}
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
+            for line in f:
+                if ":" in line and not line.lstrip().startswith("#"):
+                    k, v = line.split(":", 1)
+                    t[k.strip()] = v.strip()
+    except OSError:
         return None
     if t.get("source_sha256") != source_digest():
         return None
-    return t.get("hbm_bytes_per_launch")
+    try:
+        return float(t["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 # --------------------------------------------------------------------------- #
@@ -57,42 +65,46 @@ def measured_traffic():
 # --------------------------------------------------------------------------- #
 
 def cpu_baseline(w, target_s, reuse):
+    """The oracle on whole heads of the workload (every query row, every partition of the step).
+
+    One head is timed first; then as many further heads as fit in about ``target_s``
+    seconds are timed together, and that run is reported. Whole heads keep the
+    oracle's fixed per-head cost (upcasting the head's keys and values) in the
+    same proportion as in a full run.
+    """
     import numpy as np
     import oracle
     cores = len(os.sched_getaffinity(0))
-    nh = min(w.H, cores)
-    heads = list(range(nh))
 
-    def run(rows):
-        q = w.q[:, heads, :rows]
-        k, v = w.k[:, heads], w.v[:, heads]
+    def run(heads):
+        nh = len(heads)
         t0 = time.perf_counter()
-        o, l = oracle.partition_states(q, k, v, w.ranges, w.scale, workers=cores)
-        oracle.contribution(l.reshape(w.P, -1), rows)
-        flops = 4 * nh * rows * w.D * sum(e - s for s, e in w.ranges)
+        o, l = oracle.partition_states(w.q[:, heads], w.k[:, heads], w.v[:, heads], w.ranges, w.scale, workers=cores)
+        oracle.contribution(l.reshape(w.P, -1), w.Sq)
+        flops = 4 * nh * w.Sq * w.D * sum(e - s for s, e in w.ranges)
         if reuse:
             near_ranges = [w.ranges[i] for i in w.near]
-            o1, l1 = oracle.partition_states(w.q1[:, heads, :rows], w.k1[:, heads], w.v1[:, heads], near_ranges,
+            o1, l1 = oracle.partition_states(w.q1[:, heads], w.k1[:, heads], w.v1[:, heads], near_ranges,
                                              w.scale, workers=cores)
             full_o1 = np.zeros_like(o)
             full_l1 = np.full_like(l, -np.inf)
             full_o1[w.near], full_l1[w.near] = o1, l1
             _, _, _, c_l = oracle.selective_reuse(o, l, full_o1, full_l1, w.near)
-            oracle.contribution(np.concatenate([l1, c_l[None]]).reshape(len(w.near) + 1, -1), rows)
-            flops += 4 * nh * rows * w.D * sum(e - s for s, e in near_ranges)
+            oracle.contribution(np.concatenate([l1, c_l[None]]).reshape(len(w.near) + 1, -1), w.Sq)
+            flops += 4 * nh * w.Sq * w.D * sum(e - s for s, e in near_ranges)
         else:
             oracle.merge(o, l)
         return flops, time.perf_counter() - t0
 
-    # calibrate on two small samples (fixed cost + per-row cost), then run ~target_s seconds
-    _, ta = run(8)
-    _, tb = run(40)
-    per_row = max((tb - ta) / 32, 1e-6)
-    rows = int(max(8, min(w.Sq, (target_s - ta) / per_row + 8)))
-    flops, dt = run(rows)
+    flops, dt = run([0])
+    heads = [0]
+    more = min(w.H - 1, int((target_s - dt) / max(dt, 1e-3)))
+    if more >= 1:
+        heads = list(range(1, 1 + more))
+        flops, dt = run(heads)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{nh} of {w.H} heads x first {rows} of {w.Sq} query rows, all partitions of the step "
-                      f"(fp64 numpy, {dt:.1f} s)"}
+            "sample": f"{len(heads)} of {w.H} heads, all {w.Sq} query rows, every partition of the step "
+                      f"(fp64 numpy oracle, {dt:.1f} s)"}
 
 
 # --------------------------------------------------------------------------- #
