@@ -146,7 +146,7 @@ def random_states(seed, n, rows, D, n_empty=0):
 
 
 @pytest.mark.parametrize("n,rows,D", [(2, 1000, 128), (5, 777, 128), (32, 300, 128), (28, 129, 64), (64, 33, 4),
-                                      (3, 50, 1024)])
+                                      (3, 50, 1024), (9, 301, 32), (64, 77, 256), (17, 90, 40), (1, 20, 128)])
 def test_merge_matches_oracle(n, rows, D):
     outs, lses = random_states(n * 1000 + D, n, rows, D, n_empty=rows // 3)
     # one row where every input is empty
