@@ -102,6 +102,11 @@ def cpu_baseline(w, target_s, reuse):
     if more >= 1:
         heads = list(range(1, 1 + more))
         flops, dt = run(heads)
+        # several heads share the cores better than one: rescale once from this run
+        if dt < 0.6 * target_s and len(heads) < w.H - 1:
+            nh = min(w.H - 1, max(len(heads) + 1, int(len(heads) * target_s / max(dt, 1e-3))))
+            heads = list(range(1, 1 + nh))
+            flops, dt = run(heads)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{len(heads)} of {w.H} heads, all {w.Sq} query rows, every partition of the step "
                       f"(fp64 numpy oracle, {dt:.1f} s)"}

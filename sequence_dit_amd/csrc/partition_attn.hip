@@ -5,8 +5,7 @@
 //   partition is its partial attention output with the log-sum-exp of its scores.
 //
 // bf16 kernel design (one workgroup = 8 waves = 256 query rows x one (batch, head)
-// x one partition; one wave = 32 query rows; two waves per SIMD so that one
-// wave's softmax overlaps the other's MFMA work):
+// x one partition; one wave = 32 query rows; two waves per SIMD):
 //   * The scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16
 //     (M = 32 keys, N = 32 queries, K = 16 of D). In that accumulator layout a lane
 //     holds 16 keys of ONE query row, so the row max needs one cross-half swap
@@ -15,13 +14,17 @@
 //     O^T = V^T P^T (M = 32 of D, N = 32 queries, K = 16 keys) once rounded to bf16:
 //     P never leaves registers.
 //   * Q stays in registers for the whole partition. K tiles are staged in LDS as
-//     [key][d] with 16-byte chunks XOR-swizzled by row; V tiles are transposed on
-//     their way into LDS ([d][key], 4-key groups XOR-swizzled by d) so the V^T
-//     operand is two 8-byte LDS reads per lane. Both are double buffered: the
-//     global loads of tile t+1 are in flight while tile t is computed.
+//     [key][d] rows padded to 2D + 16 bytes; V tiles are transposed in registers on
+//     their way into LDS ([d][key] rows of 64 keys padded to 144 bytes, 4-key groups
+//     placed so that one 16-byte read per lane is the V^T operand). The padding makes
+//     the 16-byte operand reads conflict-free. Two slots per operand: the global
+//     loads of a tile are issued one tile ahead of its LDS store.
+//   * The 8 waves form two groups that alternate an MFMA phase with a softmax phase,
+//     one phase apart, so that on every SIMD one wave's softmax runs beside the
+//     other's MFMAs (a wave does not overlap its own VALU work with its MFMAs).
 //   * Online softmax in the exp2 domain with a lazy rescale: the running max is
 //     only moved (and O, l rescaled) when a new score exceeds it by more than
-//     2^8, which is exact because the same max is used for O and l.
+//     2^64, which is exact because the same max is used for O and l.
 //   * Workgroups sharing a (batch, head, partition) are mapped to the same XCD so
 //     that its L2 serves their common K/V tiles.
 #include <hip/hip_runtime.h>
@@ -37,7 +40,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 8;
 constexpr int kQB = 1;                       // 32-row query blocks per wave
@@ -45,7 +47,7 @@ constexpr int kRowsPerWave = 32 * kQB;       // 32
 constexpr int kBQ = kWaves * kRowsPerWave;   // 256 query rows per workgroup
 constexpr int kBK = 64;                      // keys per tile
 constexpr int kThreads = kWaves * 64;
-constexpr float kRescaleThreshold = 8.0f;    // log2 units
+constexpr float kRescaleThreshold = 64.0f;   // log2 units: probabilities stay <= 2^64
 
 // Maps the hardware workgroup id to a logical tile id so that consecutive logical
 // ids land on the same XCD (workgroups are dealt round-robin over the 8 XCDs).
@@ -54,19 +56,6 @@ __device__ __forceinline__ int xcd_remap(int L, int total) {
   const int per = total / kXcd, rem = total % kXcd;
   const int x = L % kXcd, idx = L / kXcd;
   return (x < rem) ? x * (per + 1) + idx : rem * (per + 1) + (x - rem) * per + idx;
-}
-
-// Swizzle of the 8-byte (4-key) groups in a row d of the transposed V tile:
-// conflict-free both for the staging writes (16 lanes on rows 8c+d') and for the
-// operand reads (16 lanes on 16 consecutive rows).
-__device__ __forceinline__ int vt_swz(int d) {
-  return ((((d & 7) ^ ((d >> 4) & 7)) << 1) | ((d >> 3) & 1));
-}
-
-__device__ __forceinline__ float swap_halves(float x) {
-  // v_permlane32_swap: returns {lanes 0-31 of x in the upper half, 32-63 in the lower}
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ float wave_max_halves(float x) {
@@ -91,9 +80,9 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Instruction classes for __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedDsRead = 0x100;
+// Operand reads in flight during an MFMA phase (one ds_read_b128 per MFMA).
+constexpr int kLookahead = 6;
+
 
 // LDS layout of one workgroup (bytes). Rows are padded by 16 bytes instead of
 // XOR-swizzled, so every operand address is a per-lane base plus a compile-time
@@ -129,51 +118,54 @@ struct Wave {
   int k_rd, v_rd;        // LDS read bases of this lane
 
   // MFMA phase of tile t: S_t = K_t Q^T from K slot KS (if DO_S) and
-  // O^T += V_{t-1}^T P_{t-1}^T from V slot VS (if DO_PV). Operand reads run six
-  // ahead of the MFMAs that consume them.
+  // O^T += V_{t-1}^T P_{t-1}^T from V slot VS (if DO_PV). S and PV steps alternate;
+  // the operand of step j + LA is read right after the MFMA of step j is issued, and
+  // a scheduling fence after every step pins that order, so that LA reads are always
+  // in flight (left to itself the scheduler moves a read next to its consumer and
+  // the wave drains the LDS queue).
   template <int KS, int VS, bool DO_S, bool DO_PV>
   __device__ __forceinline__ void mfma_phase(const char* smem) {
     using L = Lds<D>;
     constexpr int NS = DO_S ? 2 * NDS : 0;
     constexpr int NPV = DO_PV ? 4 * NDB : 0;
     constexpr int N = NS + NPV;
-    constexpr int NMAX = NS > NPV ? NS : NPV;
-    bf16x8 kf[2 * NDS > 0 ? 2 * NDS : 1];
-    bf16x8 vf[4 * NDB];
+    constexpr int NM = NS < NPV ? NS : NPV;
+    constexpr int LA = N < kLookahead ? N : kLookahead;
+    const char* kb_ = smem + k_rd + KS * L::KTILE;
+    const char* vb_ = smem + v_rd + VS * L::VTILE;
+    auto is_s = [](int j) { return NS == 0 ? false : NPV == 0 ? true : (j < 2 * NM ? (j & 1) == 0 : NS > NPV); };
+    auto idx = [](int j) { return j < 2 * NM ? j / 2 : j - NM; };
+    bf16x8 fr[N > 0 ? N : 1];
+    auto load = [&](int j) {
+      const int i = idx(j);
+      if (is_s(j)) {
+        const int ds = i >> 1, kb = i & 1;
+        fr[j] = *reinterpret_cast<const bf16x8*>(kb_ + kb * 32 * L::KP + ds * 32);
+      } else {
+        const int kbc = i / NDB, db = i % NDB;     // kbc = 2kb + c
+        fr[j] = *reinterpret_cast<const bf16x8*>(vb_ + db * 32 * L::VP + 32 * kbc);
+      }
+    };
     if (DO_S) {
       s[0] = f32x16{};
       s[1] = f32x16{};
     }
 #pragma unroll
-    for (int i = 0; i < NMAX; ++i) {
-      if (i < NS) {
-        const int ds = i >> 1, kb = i & 1;
-        kf[i] = *reinterpret_cast<const bf16x8*>(smem + k_rd + KS * L::KTILE + kb * 32 * L::KP + ds * 32);
-      }
-      if (i < NPV) {
-        const int kbc = i / NDB, db = i % NDB;     // kbc = 2kb + c
-        vf[i] = *reinterpret_cast<const bf16x8*>(smem + v_rd + VS * L::VTILE + db * 32 * L::VP + 32 * kbc);
-      }
-    }
+    for (int j = 0; j < LA; ++j) load(j);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < NMAX; ++i) {
-      if (i < NS) {
+    for (int j = 0; j < N; ++j) {
+      const int i = idx(j);
+      if (is_s(j)) {
         const int ds = i >> 1, kb = i & 1;
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[ds], s[kb], 0, 0, 0);
-      }
-      if (i < NPV) {
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j], qf[ds], s[kb], 0, 0, 0);
+      } else {
         const int kbc = i / NDB, db = i % NDB;
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[kbc >> 1][kbc & 1], o[db], 0, 0, 0);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j], pf[kbc >> 1][kbc & 1], o[db], 0, 0, 0);
       }
+      if (j + LA < N) load(j + LA);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    constexpr int LA = N < 6 ? N : 6;
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, LA, 0);
-#pragma unroll
-    for (int i = 0; i < N - LA; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, LA, 0);
   }
 
   // Softmax phase of tile t: online softmax of S_t (exp2 domain, lazy rescale) -> P_t.
@@ -183,6 +175,12 @@ struct Wave {
     else softmax<false>(valid, c2, half);
   }
 
+  // The running max m only has to keep the probabilities finite (p <= 2^64 here):
+  // floating point does not care how far below 1 they are. Each lane compares its
+  // own scores against m + 64 (one max3 chain, no cross-lane step); only when some
+  // lane exceeds it (always on the first tile, where m = -inf) does the wave take
+  // the exact row max, rescale O and l, and move m. O and l always share m, so
+  // OUT = O / l and LSE = m + log2 l are exact whichever m is used.
   template <bool MASK>
   __device__ __forceinline__ void softmax(int valid, float c2, int half) {
     if (MASK) {  // keys past the end of the partition
@@ -194,16 +192,18 @@ struct Wave {
           if (key >= valid) s[kb][r] = -INFINITY;
         }
     }
-    float x = fmaxf(s[0][0], s[1][0]);
+    float x = s[0][0];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) x = fmaxf(x, fmaxf(s[0][r], s[1][r]));
-    const float mx = wave_max_halves(x) * c2;
-    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleThreshold) != 0) {
+    for (int r = 1; r < 16; ++r) x = fmaxf(x, s[0][r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x = fmaxf(x, s[1][r]);
+    if (__builtin_amdgcn_ballot_w64(x * c2 > m + kRescaleThreshold) != 0) {
+      const float mx = wave_max_halves(x) * c2;
       const float mn = fmaxf(m, mx);
-      const float f = __builtin_amdgcn_exp2f(m - mn);
+      const float f = __builtin_amdgcn_exp2f(m - mn);   // 0 on the first tile (m = -inf)
       m = mn;
       l *= f;
-      // in-place multiplies: keeps the accumulators in their registers across the branch
+      // in-place multiplies keep the accumulators in their registers across the branch
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
