@@ -20,3 +20,4 @@ from .states import (  # noqa: F401
     partition_states,
     selective_reuse,
 )
+from . import planner  # noqa: F401  (anchor-guided planner statistics)

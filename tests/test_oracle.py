@@ -19,6 +19,7 @@ import oracle
 from sequence_dit_amd import inputs
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked_states.txt")
+GOLDEN_PLANNER = os.path.join(os.path.dirname(__file__), "golden", "hand_worked_planner.txt")
 
 
 def rand(seed, *shape):
@@ -46,6 +47,8 @@ def parse_value(s):
         return -math.inf
     if s.startswith("ln(") and s.endswith(")"):
         return math.log(Fraction(s[3:-1]))
+    if s.startswith("sqrt(") and s.endswith(")"):
+        return math.sqrt(Fraction(s[5:-1]))
     return float(Fraction(s))
 
 
@@ -226,8 +229,114 @@ def check_reuse(orc):
     assert errs[0] < 1e-25 < errs[1] < errs[2]
 
 
+# --------------------------------------------------------------------------- #
+# Planner statistics (Eqs. 9, 10, 12, 13, Algorithm 1)
+# --------------------------------------------------------------------------- #
+
+def check_planner_golden(orc):
+    g = load_golden(GOLDEN_PLANNER)
+    pl = orc.planner
+    a = np.array(g["norm_a"]).reshape(2, 2, 2)
+    b = np.array(g["norm_b"]).reshape(2, 2, 2)
+    np.testing.assert_allclose(pl.state_norm(a), g["norm_a_expected"][0], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(pl.state_norm(a, b), g["norm_diff_expected"][0], rtol=0, atol=1e-15)
+    local, group = int(g["plan_params"][0][0]), int(g["plan_params"][0][1])
+    eps, eps_local = g["plan_params"][0][2], g["plan_params"][0][3]
+    r = pl.planner(g["plan_norms"][0], g["plan_drift"][0][0], g["plan_weights"][0], local, group, eps, eps_local)
+    for key in ("alpha", "delta", "ase"):
+        np.testing.assert_allclose(r[key], g["plan_" + key][0], rtol=0, atol=1e-15)
+    assert list(r["compute"]) == [int(x) for x in g["plan_compute"][0]]
+    assert int(r["anchor"]) == int(g["plan_anchor"][0][0])
+    for frac, want in g["eps_cases"]:
+        got = pl.epsilon(g["eps_corr"][0], g["plan_weights"][0], local, group, frac)
+        assert (got == want) if math.isinf(want) else abs(got - want) < 1e-15, (frac, got, want)
+
+
+def check_norms(orc):
+    pl = orc.planner
+    a = rand(41, 3, 2, 5)
+    b = rand(42, 3, 2, 5)
+    # pure-Python loops
+    for mode in (None, b):
+        got = pl.state_norm(a, mode)
+        for i in range(3):
+            acc = 0.0
+            for r in range(2):
+                for c in range(5):
+                    d = a[i, r, c] - (0.0 if mode is None else mode[i, r, c])
+                    acc += d * d
+            assert abs(got[i] - math.sqrt(acc)) < 1e-12
+    # homogeneity, zero difference, disjoint supports (Pythagoras)
+    np.testing.assert_allclose(pl.state_norm(-3 * a), 3 * pl.state_norm(a), rtol=1e-14)
+    np.testing.assert_array_equal(pl.state_norm(a, a), np.zeros(3))
+    lo, hi = a.copy(), a.copy()
+    lo[:, :, 3:] = 0
+    hi[:, :, :3] = 0
+    np.testing.assert_allclose(pl.state_norm(a) ** 2, pl.state_norm(lo) ** 2 + pl.state_norm(hi) ** 2, rtol=1e-13)
+    np.testing.assert_allclose(pl.state_norm(lo, -hi), pl.state_norm(a), rtol=1e-14)
+
+
+def check_planner_invariants(orc):
+    pl = orc.planner
+    g = np.random.default_rng(5)
+    P, group = 11, 3                      # groups {0,1,2} {3,4,5} {6,7,8} {9,10}
+    norms = g.uniform(0.5, 4, P)
+    w = g.dirichlet(np.ones(P))
+    for local in (0, 4, 10):
+        alpha = pl.scale_ratios(norms, local)
+        assert alpha[local] == 1.0
+        np.testing.assert_allclose(pl.scale_ratios(7.5 * norms, local), alpha, rtol=1e-15)
+        np.testing.assert_allclose(alpha * norms[local], norms, rtol=1e-15)
+        d1 = pl.drift_errors(alpha, 0.3)
+        np.testing.assert_allclose(pl.drift_errors(alpha, 0.6), 2 * d1, rtol=1e-15)
+        np.testing.assert_allclose(d1[local], 0.3, rtol=1e-15)
+        ase = pl.group_errors(w, d1, group)
+        assert len(ase) == 4
+        np.testing.assert_allclose(ase[3], w[9] * d1[9] + w[10] * d1[10], rtol=1e-15)
+        np.testing.assert_allclose(ase.sum(), np.dot(w, d1), rtol=1e-14)
+        # raising one weight raises exactly its group's error
+        w2 = w.copy()
+        w2[7] += 0.5
+        diff = pl.group_errors(w2, d1, group) - ase
+        assert diff[2] > 0 and np.all(diff[[0, 1, 3]] == 0)
+        # no drift: every non-local group is reused; -inf threshold: everything computed
+        z = pl.planner(norms, 0.0, w, local, group, 0.0, 1.0)
+        assert np.all(z["ase"] == 0) and list(z["compute"]) == [int(k == local // group) for k in range(4)]
+        assert not z["anchor"] and pl.planner(norms, 2.0, w, local, group, 0.0, 1.0)["anchor"]
+        assert list(pl.decide(ase, local, group, -math.inf)) == [1, 1, 1, 1]
+        # a threshold between two errors splits the non-local groups by their error
+        c = pl.decide(ase, local, group, float(np.median(ase)))
+        for k in range(4):
+            assert c[k] == (1 if k == local // group else int(ase[k] > np.median(ase)))
+
+
+def check_epsilon(orc):
+    pl = orc.planner
+    g = np.random.default_rng(9)
+    P, group, local = 32, 4, 16            # 8 groups, local group 4, G' = 7
+    corr = g.uniform(0, 1, P)
+    w = g.dirichlet(np.ones(P))
+    E = pl.group_errors(w, corr, group)
+    others = np.delete(E, local // group)
+    prev = -math.inf
+    for R in (0.0, 0.1, 0.15, 1 / 7, 0.3, 0.5, 0.75, 0.99, 1.0):
+        eps = pl.epsilon(corr, w, local, group, R)
+        m = int(np.floor(np.float32(R) * np.float32(7)))
+        assert int(np.sum(others <= eps)) == m, (R, eps)
+        assert eps >= prev
+        prev = eps
+        if m:
+            assert eps in list(others)
+        # planning with the threshold on the correction errors reuses exactly m groups
+        c = pl.decide(E, local, group, eps)
+        assert c[local // group] == 1 and int(np.sum(c == 0)) == m
+    assert pl.epsilon(corr, w, local, group, 1.0) == others.max()
+    assert pl.epsilon(corr, w, local, group, 0.0) == -math.inf
+
+
 PINS = [check_golden, check_bruteforce_loops, check_states_vs_sdpa, check_merge_equals_full,
-        check_identity_bitexact, check_closed_forms, check_contribution, check_reuse]
+        check_identity_bitexact, check_closed_forms, check_contribution, check_reuse,
+        check_planner_golden, check_norms, check_planner_invariants, check_epsilon]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -286,6 +395,7 @@ def test_smooth_component_gives_spatial_locality():
 # --------------------------------------------------------------------------- #
 
 MUTANTS = {
+    # states.py
     "scale dropped": ("z = scale * (q @ k.T)", "z = (q @ k.T)"),
     "keys used as values": ("return p @ v, lse", "return p @ k, lse"),
     "head index mixed up": ("k[b, h, s:e], v[b, h, s:e]", "k[b, -1 - h, s:e], v[b, -1 - h, s:e]"),
@@ -300,16 +410,38 @@ MUTANTS = {
     "reuse caches the new step": ("c_out, c_lse = merge(out_t[far], lse_t[far])",
                                   "c_out, c_lse = merge(_f64(out_t1)[far], _f64(lse_t1)[far])"),
     "range end off by one": ("k[b, h, s:e], v[b, h, s:e]", "k[b, h, s:e + 1], v[b, h, s:e + 1]"),
+    # planner.py
+    "alpha inverted": ("return n / n[local]", "return n[local] / n", "planner.py"),
+    "drift not scaled by alpha": ("return _f64(alpha) * float(local_drift)",
+                                  "return np.ones_like(_f64(alpha)) * float(local_drift)", "planner.py"),
+    "group boundary off by one": ("range(k, min(k + group, P))", "range(k, min(k + group + 1, P))", "planner.py"),
+    "weights left out of ASE": ("sum(w[j] * d[j] for j in g)", "sum(d[j] for j in g)", "planner.py"),
+    "local group not forced": ("compute[local // group] = 1", "pass", "planner.py"),
+    "reuse above the threshold": ("compute = (ase > eps)", "compute = (ase < eps)", "planner.py"),
+    "percentile off by one": ("np.sort(others)[m - 1]", "np.sort(others)[min(m, len(others) - 1)]", "planner.py"),
+    "local group kept in percentile": ("if k != local // group]", "if True]", "planner.py"),
+    "norm left squared": ("return np.sqrt(np.einsum(\"ij,ij->i\", d, d))", "return np.einsum(\"ij,ij->i\", d, d)",
+                          "planner.py"),
+    "difference taken as a sum": ("d = a if b is None else a - _f64(b)", "d = a if b is None else a + _f64(b)",
+                                  "planner.py"),
+    "anchor on small drift": ("return float(local_drift) > float(eps_local)",
+                              "return float(local_drift) < float(eps_local)", "planner.py"),
 }
 
 
-def mutant_module(old, new):
-    src_path = os.path.join(os.path.dirname(oracle.__file__), "states.py")
+def mutant_module(old, new, file="states.py"):
+    """A stand-in for the oracle package with `old` replaced by `new` in one of its sources."""
+    src_path = os.path.join(os.path.dirname(oracle.__file__), file)
     src = open(src_path).read()
     assert src.count(old) == 1, old
-    mod = types.ModuleType("oracle_mutant")
+    mod = types.ModuleType("oracle_mutant_" + file[:-3])
     mod.__file__ = src_path
     exec(compile(src.replace(old, new), src_path, "exec"), mod.__dict__)
+    if file == "planner.py":
+        pkg = types.SimpleNamespace(**{k: getattr(oracle, k) for k in dir(oracle) if not k.startswith("_")})
+        pkg.planner = mod
+        return pkg
+    mod.planner = oracle.planner
     return mod
 
 
