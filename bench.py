@@ -123,7 +123,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=5, choices=[2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=22.0)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy (y = x * 1, fp32) reading and writing this many MiB, "
                          "outside the timed region, to calibrate HBM byte counters")
@@ -238,6 +238,30 @@ def main():
         by = 2 * P * rows * 4
         kernels[n] = {"P": P, "ms": round(ms, 4), "GB/s": round(by / ms / 1e6, 1)}
     merge_gbps = merge_bytes_total / (merge_ms_total * 1e-3) / 1e9
+
+    if reuse:
+        # planner statistics (timed on their own, outside the step): anchor norms of every
+        # partition's OUT, global weights, the local drift and the decision
+        eps = torch.tensor([1e-4], dtype=torch.float32, device=dev)
+        runner.timer = None
+        runner.plan_anchor()
+        runner.plan_step(w.local, 4, eps, 0.5)
+        torch.cuda.synchronize()
+        runner.timer = []
+        for _ in range(args.steps):
+            runner.plan_anchor()
+            runner.plan_step(w.local, 4, eps, 0.5)
+        torch.cuda.synchronize()
+        ptimes = {}
+        for name, s, e in runner.timer:
+            ptimes.setdefault(name, []).append(s.elapsed_time(e))
+        n_state = rows * w.D
+        for name, by in (("plan_norms_anchor", w.P * n_state * 4), ("plan_drift", 2 * n_state * 4),
+                         ("plan_weights", w.P * rows * 4), ("plan_decide", None)):
+            ms = sum(ptimes[name]) / len(ptimes[name])
+            kernels[name] = {"ms": round(ms, 4)}
+            if by:
+                kernels[name].update({"GB/s": round(by / ms / 1e6, 1), "frac_hbm": round(by / ms / 1e6 / PEAK_HBM_GBPS, 4)})
 
     traffic = measured_traffic()
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

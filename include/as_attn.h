@@ -135,6 +135,89 @@ as_status as_partition_contribution(const float* lse, int32_t P, int64_t rows, i
                                     float* weights, float* scores, void* workspace,
                                     size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Anchor-guided planner statistics.
+ *   Source: DiTango review page (pith.science): "What carries the argument" (the
+ *   group error ASE(G_i, t) = sum over the group of w(j, t) * delta(j, t, t_c), Eq. 12),
+ *   the free-parameter ledger (scale ratio alpha(i) = ||AS_ta(i)|| / ||AS_ta(i_loc)||,
+ *   Eq. 9; group size g; local threshold eps_local and percentile threshold eps of
+ *   Algorithm 1) and the referee report on section 4.1.2 (drift model
+ *   delta(i, t, t_a) = alpha(i) * ||AS_t(i_loc) - AS_ta(i_loc)||, Eq. 10, and the
+ *   reuse decision of Eq. 13).
+ *   ||AS|| is taken as the L2 norm of the OUT part of a state over the whole query
+ *   shard (LSE excluded).
+ */
+
+/*
+ * as_state_norms_workspace_size - bytes of device workspace as_state_norms needs
+ * for these sizes (one fp64 partial sum per chunk of each slice). Returns 0 for
+ * invalid sizes.
+ */
+size_t as_state_norms_workspace_size(int32_t P, int64_t n);
+
+/*
+ * as_state_norms - L2 norms of P state slices or of their differences:
+ *   norms[i] = sqrt(sum_e (a[i][e] - b[i][e])^2),   or sqrt(sum_e a[i][e]^2) if b is NULL.
+ * Differences and squares are formed and summed in fp64 in a fixed order, so the
+ * result (rounded to fp32) is bitwise reproducible.
+ *
+ * a, b       DEVICE float32 [P][n], contiguous (slice i starts at element i*n),
+ *            16-byte aligned; b may be NULL. For a1's output, a slice is one
+ *            partition's OUT: n = B*H*Sq*D.
+ * P          1 <= P <= AS_MAX_PARTITIONS.
+ * n          >= 0 and a multiple of 4. n == 0 gives norms of 0.
+ * norms      DEVICE float32 [P], 4-byte aligned.
+ * workspace  DEVICE buffer of at least as_state_norms_workspace_size(P, n) bytes,
+ *            16-byte aligned; its contents on entry do not matter.
+ */
+as_status as_state_norms(const float* a, const float* b, int32_t P, int64_t n, float* norms,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * as_planner_decide - one planning step. Partitions form contiguous groups of
+ * `group`: group k holds partitions k*group .. min((k+1)*group, P) - 1 (the last
+ * group may be shorter); the local group is local / group. With d = local_drift[0]:
+ *   alpha[i]   = anchor_norms[i] / anchor_norms[local]                  (Eq. 9)
+ *   delta[i]   = alpha[i] * d                                           (Eq. 10)
+ *   ase[k]     = sum over j in group k of weights[j] * delta[j]         (Eq. 12)
+ *   compute[k] = 1 if k is the local group or ase[k] > eps[0], else 0   (Eq. 13: 0 = reuse)
+ *   anchor[0]  = 1 if d > eps_local, else 0     (Algorithm 1: a new anchor step is due)
+ * fp32 arithmetic; group sums in ascending partition order.
+ *
+ * anchor_norms  DEVICE float32 [P]: ||OUT_ta(i)|| (as_state_norms on the anchor step's
+ *               states); anchor_norms[local] must be > 0.
+ * local_drift   DEVICE float32 [1]: ||OUT_t(local) - OUT_ta(local)|| (as_state_norms, P = 1).
+ * weights       DEVICE float32 [P]: w(i) of the anchor step (as_partition_contribution
+ *               scores with one group of all rows).
+ * eps           DEVICE float32 [1]: the reuse threshold (as_planner_epsilon or the caller's).
+ * P, local      1 <= P <= AS_MAX_PARTITIONS, 0 <= local < P.   group >= 1.
+ * eps_local     finite.
+ * alpha, delta  DEVICE float32 [P] or NULL (not written).   ase: DEVICE float32 [G] or NULL.
+ * compute       DEVICE int32 [G], G = ceil(P / group).   anchor: DEVICE int32 [1].
+ */
+as_status as_planner_decide(const float* anchor_norms, const float* local_drift, const float* weights,
+                            const float* eps, int32_t P, int32_t local, int32_t group, float eps_local,
+                            float* alpha, float* delta, float* ase, int32_t* compute, int32_t* anchor,
+                            hipStream_t stream);
+
+/*
+ * as_planner_epsilon - the reuse threshold of Algorithm 1 from anchor correction errors.
+ *   E[k]   = sum over j in group k of weights[j] * corr_norms[j]   (groups as above)
+ *   m      = floor(float(reuse_fraction) * float(G')) over the G' = G - 1 non-local
+ *            groups (float32 product)
+ *   eps[0] = the m-th smallest E[k] over the non-local groups (ties broken by group
+ *            index), or -inf when m == 0 (nothing is reused).
+ * With this eps, m non-local groups have E[k] <= eps.
+ *
+ * corr_norms      DEVICE float32 [P]: ||OUT_ta(j) - OUT_tc(j)|| between the anchor step's
+ *                 fresh states and the states cached before it (as_state_norms).
+ * weights         DEVICE float32 [P] (as in as_planner_decide).
+ * reuse_fraction  target fraction of the non-local groups to reuse, 0 <= R <= 1.
+ * eps             DEVICE float32 [1].
+ */
+as_status as_planner_epsilon(const float* corr_norms, const float* weights, int32_t P, int32_t local,
+                             int32_t group, float reuse_fraction, float* eps, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* as_status_string(as_status s);
 

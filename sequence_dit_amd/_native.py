@@ -22,7 +22,8 @@ AS_MAX_PARTITIONS = 256
 AS_MAX_MERGE = 64
 
 EXPORTS = ("as_partition_attn", "as_merge", "as_partition_contribution_workspace_size",
-           "as_partition_contribution", "as_status_string", "as_last_error")
+           "as_partition_contribution", "as_state_norms_workspace_size", "as_state_norms",
+           "as_planner_decide", "as_planner_epsilon", "as_status_string", "as_last_error")
 
 _lib = None
 
@@ -66,6 +67,19 @@ def lib() -> ctypes.CDLL:
         L.as_partition_contribution.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                                 ctypes.c_void_p]
+        L.as_state_norms_workspace_size.restype = ctypes.c_size_t
+        L.as_state_norms_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int64]
+        L.as_state_norms.restype = ctypes.c_int
+        L.as_state_norms.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.as_planner_decide.restype = ctypes.c_int
+        L.as_planner_decide.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p]
+        L.as_planner_epsilon.restype = ctypes.c_int
+        L.as_planner_epsilon.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
         L.as_status_string.restype = ctypes.c_char_p
         L.as_status_string.argtypes = [ctypes.c_int]
         L.as_last_error.restype = ctypes.c_char_p
@@ -195,3 +209,72 @@ def partition_contribution(lse: torch.Tensor, rows_per_group: int, want_weights:
                                           workspace.data_ptr() if workspace is not None else None,
                                           ws_bytes, _stream(lse)))
     return w, s
+
+
+# --------------------------------------------------------------------------- #
+# Planner statistics: as_state_norms, as_planner_decide, as_planner_epsilon
+# --------------------------------------------------------------------------- #
+
+def state_norms_workspace_size(P: int, n: int) -> int:
+    return int(lib().as_state_norms_workspace_size(P, n))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return t.data_ptr() if t is not None else None
+
+
+def state_norms(a: torch.Tensor, b: Optional[torch.Tensor] = None, norms: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """||a_i|| (or ||a_i - b_i||) for every slice i of a [P, ...] float32; returns norms [P] float32."""
+    _require_gpu(a, *([b] if b is not None else []))
+    if a.dtype != torch.float32 or not a.is_contiguous() or a.dim() < 1:
+        raise ValueError("a must be a contiguous float32 tensor [P, ...]")
+    if b is not None and (b.dtype != torch.float32 or not b.is_contiguous() or b.shape != a.shape):
+        raise ValueError("b must be a contiguous float32 tensor shaped like a")
+    P = a.shape[0]
+    n = a.numel() // max(P, 1)
+    if norms is None:
+        norms = torch.empty(P, dtype=torch.float32, device=a.device)
+    need = state_norms_workspace_size(P, n)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=a.device)
+    check(lib().as_state_norms(a.data_ptr(), _ptr(b), P, n, norms.data_ptr(), workspace.data_ptr(),
+                               workspace.numel() * workspace.element_size(), _stream(a)))
+    return norms
+
+
+def planner_decide(anchor_norms: torch.Tensor, local_drift: torch.Tensor, weights: torch.Tensor,
+                   eps: torch.Tensor, local: int, group: int, eps_local: float, want_stats: bool = True) -> dict:
+    """One planning step (alpha, delta, group errors, compute flags, anchor flag), on the device."""
+    _require_gpu(anchor_norms, local_drift, weights, eps)
+    for t in (anchor_norms, local_drift, weights, eps):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("planner inputs must be contiguous float32")
+    P = anchor_norms.numel()
+    G = (P + group - 1) // max(group, 1)
+    dev = anchor_norms.device
+    r = {"compute": torch.empty(max(G, 1), dtype=torch.int32, device=dev),
+         "anchor": torch.empty(1, dtype=torch.int32, device=dev)}
+    if want_stats:
+        r["alpha"] = torch.empty(P, dtype=torch.float32, device=dev)
+        r["delta"] = torch.empty(P, dtype=torch.float32, device=dev)
+        r["ase"] = torch.empty(max(G, 1), dtype=torch.float32, device=dev)
+    check(lib().as_planner_decide(anchor_norms.data_ptr(), local_drift.data_ptr(), weights.data_ptr(),
+                                  eps.data_ptr(), P, local, group, float(eps_local), _ptr(r.get("alpha")),
+                                  _ptr(r.get("delta")), _ptr(r.get("ase")), r["compute"].data_ptr(),
+                                  r["anchor"].data_ptr(), _stream(anchor_norms)))
+    return r
+
+
+def planner_epsilon(corr_norms: torch.Tensor, weights: torch.Tensor, local: int, group: int,
+                    reuse_fraction: float, eps: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Reuse threshold of the anchor step from per-partition correction norms; returns eps [1]."""
+    _require_gpu(corr_norms, weights)
+    for t in (corr_norms, weights):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("planner inputs must be contiguous float32")
+    if eps is None:
+        eps = torch.empty(1, dtype=torch.float32, device=corr_norms.device)
+    check(lib().as_planner_epsilon(corr_norms.data_ptr(), weights.data_ptr(), corr_norms.numel(), local, group,
+                                   float(reuse_fraction), eps.data_ptr(), _stream(corr_norms)))
+    return eps

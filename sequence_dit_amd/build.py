@@ -21,7 +21,7 @@ LIB_NAME = "libas_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "partition_attn.hip", "merge.hip", "contribution.hip"]
+SOURCES = ["api.hip", "partition_attn.hip", "merge.hip", "contribution.hip", "planner.hip"]
 
 # Per-source flags. The attention kernels never see NaN (finite inputs, -inf only
 # as a max/exp operand), so NaN-honouring max and IEEE-mode operand

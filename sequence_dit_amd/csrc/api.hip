@@ -173,4 +173,77 @@ as_status as_partition_contribution(const float* lse, int32_t P, int64_t rows, i
   return hip_status(as::launch_contribution(a, stream), "partition_contribution launch");
 }
 
+
+size_t as_state_norms_workspace_size(int32_t P, int64_t n) {
+  if (P < 1 || P > AS_MAX_PARTITIONS || n < 0 || n % 4 || n > ((int64_t)1 << 40)) return 0;
+  return (size_t)(P * as::norms_chunks(P, n)) * sizeof(double);
+}
+
+as_status as_state_norms(const float* a, const float* b, int32_t P, int64_t n, float* norms,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (P < 1 || P > AS_MAX_PARTITIONS) return fail(AS_ERR_INVALID_ARG, "P=%d outside [1, %d]", P, AS_MAX_PARTITIONS);
+  if (n < 0 || n % 4) return fail(AS_ERR_INVALID_ARG, "n=%lld must be a non-negative multiple of 4", (long long)n);
+  if (n > ((int64_t)1 << 40)) return fail(AS_ERR_UNSUPPORTED, "n=%lld too large", (long long)n);
+  if (!norms) return fail(AS_ERR_INVALID_ARG, "norms is NULL");
+  if (n > 0 && !a) return fail(AS_ERR_INVALID_ARG, "a is NULL");
+  if (!aligned(a, 16) || !aligned(b, 16)) return fail(AS_ERR_INVALID_ARG, "a and b must be 16-byte aligned");
+  if (!aligned(norms, 4)) return fail(AS_ERR_INVALID_ARG, "misaligned norms");
+  const size_t need = as_state_norms_workspace_size(P, n);
+  if (!workspace) return fail(AS_ERR_INVALID_ARG, "workspace is NULL");
+  if (workspace_bytes < need)
+    return fail(AS_ERR_INVALID_ARG, "workspace of %zu bytes is smaller than the %zu bytes needed", workspace_bytes, need);
+  if (!aligned(workspace, 16)) return fail(AS_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  as::NormArgs g;
+  memset(&g, 0, sizeof(g));
+  g.a = a; g.b = (n > 0) ? b : nullptr; g.norms = norms; g.partial = static_cast<double*>(workspace);
+  g.n = n; g.chunk = as::norms_chunk(P, n); g.P = P; g.chunks = (int32_t)as::norms_chunks(P, n);
+  return hip_status(as::launch_state_norms(g, stream), "state_norms launch");
+}
+
+namespace {
+as_status check_groups(int32_t P, int32_t local, int32_t group) {
+  if (P < 1 || P > AS_MAX_PARTITIONS) return fail(AS_ERR_INVALID_ARG, "P=%d outside [1, %d]", P, AS_MAX_PARTITIONS);
+  if (local < 0 || local >= P) return fail(AS_ERR_INVALID_ARG, "local=%d outside [0, P=%d)", local, P);
+  if (group < 1) return fail(AS_ERR_INVALID_ARG, "group=%d must be >= 1", group);
+  return AS_OK;
+}
+}  // namespace
+
+as_status as_planner_decide(const float* anchor_norms, const float* local_drift, const float* weights,
+                            const float* eps, int32_t P, int32_t local, int32_t group, float eps_local,
+                            float* alpha, float* delta, float* ase, int32_t* compute, int32_t* anchor,
+                            hipStream_t stream) {
+  const as_status st = check_groups(P, local, group);
+  if (st != AS_OK) return st;
+  if (!isfinite(eps_local)) return fail(AS_ERR_INVALID_ARG, "eps_local must be finite");
+  if (!anchor_norms || !local_drift || !weights || !eps || !compute || !anchor)
+    return fail(AS_ERR_INVALID_ARG, "anchor_norms, local_drift, weights, eps, compute and anchor must not be NULL");
+  const void* ptrs[] = {anchor_norms, local_drift, weights, eps, alpha, delta, ase, compute, anchor};
+  for (const void* p : ptrs)
+    if (!aligned(p, 4)) return fail(AS_ERR_INVALID_ARG, "misaligned pointer");
+  as::PlanArgs g;
+  memset(&g, 0, sizeof(g));
+  g.anchor_norms = anchor_norms; g.local_drift = local_drift; g.weights = weights; g.eps = eps;
+  g.alpha = alpha; g.delta = delta; g.ase = ase; g.compute = compute; g.anchor = anchor;
+  g.P = P; g.local = local; g.eps_local = eps_local;
+  g.group = group > P ? P : group;   // a group of more than P partitions is one group of P
+  return hip_status(as::launch_planner_decide(g, stream), "planner_decide launch");
+}
+
+as_status as_planner_epsilon(const float* corr_norms, const float* weights, int32_t P, int32_t local,
+                             int32_t group, float reuse_fraction, float* eps, hipStream_t stream) {
+  const as_status st = check_groups(P, local, group);
+  if (st != AS_OK) return st;
+  if (!(reuse_fraction >= 0.f && reuse_fraction <= 1.f))
+    return fail(AS_ERR_INVALID_ARG, "reuse_fraction=%g outside [0, 1]", (double)reuse_fraction);
+  if (!corr_norms || !weights || !eps) return fail(AS_ERR_INVALID_ARG, "corr_norms, weights and eps must not be NULL");
+  if (!aligned(corr_norms, 4) || !aligned(weights, 4) || !aligned(eps, 4))
+    return fail(AS_ERR_INVALID_ARG, "misaligned pointer");
+  as::PlanArgs g;
+  memset(&g, 0, sizeof(g));
+  g.corr_norms = corr_norms; g.weights = weights; g.eps_out = eps;
+  g.P = P; g.local = local; g.reuse_fraction = reuse_fraction;
+  g.group = group > P ? P : group;
+  return hip_status(as::launch_planner_epsilon(g, stream), "planner_epsilon launch");
+}
 }  // extern "C"

@@ -55,6 +55,51 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 
+// State norms: slice i of n floats is split into chunks of norms_chunk(P, n)
+// elements (a multiple of 1024, so every thread of a 256-thread workgroup reads
+// whole 16-byte vectors); one fp64 partial per (slice, chunk) goes to the workspace.
+struct NormArgs {
+  const float* a;      // [P][n]
+  const float* b;      // [P][n] or null
+  float* norms;        // [P]
+  double* partial;     // [P][chunks]
+  int64_t n;
+  int64_t chunk;
+  int32_t P;
+  int32_t chunks;
+};
+
+inline int64_t norms_chunk(int32_t P, int64_t n) {
+  int64_t c = (n * P + 2047) / 2048;            // about 2048 workgroups in all
+  c = (c + 1023) / 1024 * 1024;
+  return c < 4096 ? 4096 : (c > 262144 ? 262144 : c);
+}
+inline int64_t norms_chunks(int32_t P, int64_t n) {
+  const int64_t c = norms_chunk(P, n);
+  return n == 0 ? 1 : (n + c - 1) / c;
+}
+
+struct PlanArgs {
+  const float* anchor_norms;   // decide: [P]
+  const float* local_drift;    // decide: [1]
+  const float* corr_norms;     // epsilon: [P]
+  const float* weights;        // [P]
+  const float* eps;            // decide: [1]
+  float* alpha;                // decide: [P] or null
+  float* delta;                // decide: [P] or null
+  float* ase;                  // decide: [G] or null
+  int32_t* compute;            // decide: [G]
+  int32_t* anchor;             // decide: [1]
+  float* eps_out;              // epsilon: [1]
+  int32_t P, local, group;
+  float eps_local;
+  float reuse_fraction;
+};
+
+hipError_t launch_state_norms(const NormArgs& a, hipStream_t stream);
+hipError_t launch_planner_decide(const PlanArgs& a, hipStream_t stream);
+hipError_t launch_planner_epsilon(const PlanArgs& a, hipStream_t stream);
+
 // Contribution: rows are processed in chunks of this many rows per workgroup.
 constexpr int kContribChunk = 256;
 hipError_t launch_contribution(const ContribArgs& a, hipStream_t stream);

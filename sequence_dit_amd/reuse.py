@@ -5,7 +5,9 @@ at an anchor step every partition's state is computed; the states of the
 remote (low-contribution) partitions are composed into one cached state; at the
 following steps only the near partitions are recomputed and composed with the
 cached state. The partition weights (Eq. 8, softmax of LSE over partitions) are
-refreshed at the anchor.
+refreshed at the anchor. The anchor-guided planner statistics (scale ratios,
+drift model, group errors and the compute/reuse decision of Eqs. 9, 10, 12, 13)
+are computed from the same buffers by ``plan_anchor`` and ``plan_step``.
 
 Everything here is buffer management and ordering on the current torch stream;
 each step of the arithmetic runs in the HIP library (``_native``).
@@ -53,6 +55,16 @@ class SelectiveReuse:
         ws = max(_native.contribution_workspace_size(self.P, self.rows, self.rows_per_group),
                  _native.contribution_workspace_size(nf + 1, self.rows, self.rows_per_group), 16)
         self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
+        # planner: per-partition OUT norms and global weights at the anchor, local drift per step
+        self.anchor_norms = torch.empty(self.P, **f32)
+        self.global_weights = torch.empty((1, self.P), **f32)
+        self.local_drift = torch.empty(1, **f32)
+        n = self.rows * D
+        self.norms_workspace = torch.empty(max(_native.state_norms_workspace_size(self.P, n),
+                                               _native.state_norms_workspace_size(1, n), 16),
+                                           dtype=torch.uint8, device=device)
+        self.global_workspace = torch.empty(max(_native.contribution_workspace_size(self.P, self.rows, self.rows), 16),
+                                            dtype=torch.uint8, device=device)
 
     @property
     def cached_out(self) -> torch.Tensor:
@@ -89,6 +101,26 @@ class SelectiveReuse:
                     [self.step_lse[j] for j in range(nf + 1)], out=self.result_out, lse=self.result_lse)
         self._timed("contrib_step", self._contribution, self.step_lse, self.step_weights, self.step_scores)
         return self.result_out, self.result_lse
+
+    def plan_anchor(self) -> None:
+        """Planner statistics of the anchor step: ||OUT(i)|| per partition and the global weights w(i)."""
+        self._timed("plan_norms_anchor", _native.state_norms, self.state_out.view(self.P, -1),
+                    norms=self.anchor_norms, workspace=self.norms_workspace)
+        self._timed("plan_weights", self._global_weights)
+
+    def plan_step(self, local: int, group: int, eps: torch.Tensor, eps_local: float) -> dict:
+        """Planner decision at a reuse step: drift of the fresh local state from its anchor state, then
+        alpha, delta, group errors and the per-group compute flags (the local partition must be near)."""
+        fresh = self.step_out[self.near.index(local)]
+        self._timed("plan_drift", _native.state_norms, fresh.view(1, -1), self.state_out[local].view(1, -1),
+                    norms=self.local_drift, workspace=self.norms_workspace)
+        return self._timed("plan_decide", _native.planner_decide, self.anchor_norms, self.local_drift,
+                           self.global_weights.view(-1), eps, local, group, eps_local)
+
+    def _global_weights(self) -> None:
+        _native.check(_native.lib().as_partition_contribution(
+            self.state_lse.data_ptr(), self.P, self.rows, self.rows, None, self.global_weights.data_ptr(),
+            self.global_workspace.data_ptr(), self.global_workspace.numel(), _native._stream(self.state_lse)))
 
     def _contribution(self, lse: torch.Tensor, weights: torch.Tensor, scores: torch.Tensor) -> None:
         P = lse.shape[0]

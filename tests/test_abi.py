@@ -162,3 +162,95 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="HIP device"):
         N.partition_attn(x, x, x, [(0, 4)])
+
+
+def test_state_norms_workspace_size():
+    L = N.lib()
+    # 32 partitions of a long-video shard (24 * 3840 rows x 128): chunks of 184320 floats -> 64 per slice
+    n = 24 * 3840 * 128
+    assert L.as_state_norms_workspace_size(32, n) == 32 * 64 * 8
+    assert L.as_state_norms_workspace_size(1, 8) == 8            # one chunk
+    assert L.as_state_norms_workspace_size(3, 0) == 3 * 8         # n = 0 still writes a zero partial
+    assert L.as_state_norms_workspace_size(2, 6) == 0             # n not a multiple of 4
+    assert L.as_state_norms_workspace_size(0, 8) == 0
+    assert L.as_state_norms_workspace_size(257, 8) == 0
+
+
+def norms_call(a=FAKE, b=0, P=2, n=1024, out=FAKE, ws=FAKE, wsb=1 << 20):
+    st = N.lib().as_state_norms(a, b, P, n, out, ws, wsb, None)
+    return st, N.lib().as_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(P=0), N.AS_ERR_INVALID_ARG, "P=0"),
+    (dict(P=300), N.AS_ERR_INVALID_ARG, "P=300"),
+    (dict(n=-4), N.AS_ERR_INVALID_ARG, "multiple of 4"),
+    (dict(n=10), N.AS_ERR_INVALID_ARG, "multiple of 4"),
+    (dict(out=0), N.AS_ERR_INVALID_ARG, "norms is NULL"),
+    (dict(a=0), N.AS_ERR_INVALID_ARG, "a is NULL"),
+    (dict(a=FAKE + 4), N.AS_ERR_INVALID_ARG, "16-byte"),
+    (dict(b=FAKE + 8), N.AS_ERR_INVALID_ARG, "16-byte"),
+    (dict(ws=0), N.AS_ERR_INVALID_ARG, "workspace is NULL"),
+    (dict(wsb=8), N.AS_ERR_INVALID_ARG, "smaller"),
+    (dict(ws=FAKE + 8), N.AS_ERR_INVALID_ARG, "aligned"),
+])
+def test_state_norms_rejects(kw, status, text):
+    st, msg = norms_call(**kw)
+    assert st == status, msg
+    assert text in msg
+
+
+def decide_call(an=FAKE, dr=FAKE, w=FAKE, eps=FAKE, P=8, local=3, group=2, eps_local=0.5,
+                alpha=FAKE, delta=FAKE, ase=FAKE, comp=FAKE, anch=FAKE):
+    st = N.lib().as_planner_decide(an, dr, w, eps, P, local, group, eps_local, alpha, delta, ase, comp, anch, None)
+    return st, N.lib().as_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(P=0), N.AS_ERR_INVALID_ARG, "P=0"),
+    (dict(local=8), N.AS_ERR_INVALID_ARG, "local=8"),
+    (dict(local=-1), N.AS_ERR_INVALID_ARG, "local=-1"),
+    (dict(group=0), N.AS_ERR_INVALID_ARG, "group=0"),
+    (dict(eps_local=float("inf")), N.AS_ERR_INVALID_ARG, "eps_local"),
+    (dict(eps_local=float("nan")), N.AS_ERR_INVALID_ARG, "eps_local"),
+    (dict(an=0), N.AS_ERR_INVALID_ARG, "must not be NULL"),
+    (dict(eps=0), N.AS_ERR_INVALID_ARG, "must not be NULL"),
+    (dict(comp=0), N.AS_ERR_INVALID_ARG, "must not be NULL"),
+    (dict(anch=0), N.AS_ERR_INVALID_ARG, "must not be NULL"),
+    (dict(ase=FAKE + 2), N.AS_ERR_INVALID_ARG, "misaligned"),
+])
+def test_planner_decide_rejects(kw, status, text):
+    st, msg = decide_call(**kw)
+    assert st == status, msg
+    assert text in msg
+
+
+def epsilon_call(corr=FAKE, w=FAKE, P=8, local=3, group=2, R=0.5, eps=FAKE):
+    st = N.lib().as_planner_epsilon(corr, w, P, local, group, R, eps, None)
+    return st, N.lib().as_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(P=257), N.AS_ERR_INVALID_ARG, "P=257"),
+    (dict(local=9), N.AS_ERR_INVALID_ARG, "local=9"),
+    (dict(group=-1), N.AS_ERR_INVALID_ARG, "group=-1"),
+    (dict(R=-0.1), N.AS_ERR_INVALID_ARG, "reuse_fraction"),
+    (dict(R=1.5), N.AS_ERR_INVALID_ARG, "reuse_fraction"),
+    (dict(R=float("nan")), N.AS_ERR_INVALID_ARG, "reuse_fraction"),
+    (dict(corr=0), N.AS_ERR_INVALID_ARG, "must not be NULL"),
+    (dict(eps=0), N.AS_ERR_INVALID_ARG, "must not be NULL"),
+    (dict(w=FAKE + 1), N.AS_ERR_INVALID_ARG, "misaligned"),
+])
+def test_planner_epsilon_rejects(kw, status, text):
+    st, msg = epsilon_call(**kw)
+    assert st == status, msg
+    assert text in msg
+
+
+def test_planner_bindings_refuse_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 8)
+    with pytest.raises(ValueError, match="HIP device"):
+        N.state_norms(x)
+    with pytest.raises(ValueError, match="HIP device"):
+        N.planner_epsilon(x[0], x[1], 0, 2, 0.5)

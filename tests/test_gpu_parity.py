@@ -214,6 +214,81 @@ def test_contribution_matches_oracle(P, rows, rpg):
 
 
 # --------------------------------------------------------------------------- #
+# Planner statistics
+# --------------------------------------------------------------------------- #
+
+NORM_RTOL = 1e-6   # fp64 sums rounded once to fp32 (unit roundoff 2^-24)
+PLAN_RTOL = 1e-5   # fp32 arithmetic on a few terms per output
+
+
+@pytest.mark.parametrize("diff", [False, True])
+@pytest.mark.parametrize("P,n", [(1, 4), (3, 4100), (5, 0), (32, 300 * 128), (256, 64), (2, 3 * 262144 + 20),
+                                 (1, 24 * 3840 * 128)])
+def test_state_norms_matches_oracle(P, n, diff):
+    g = np.random.default_rng(P * 13 + n + int(diff))
+    a = g.standard_normal((P, n)).astype(np.float32)
+    b = g.standard_normal((P, n)).astype(np.float32) if diff else None
+    note(f"state norms P={P} n={n} diff={diff}")
+    ad = to_dev(torch.from_numpy(a))
+    bd = to_dev(torch.from_numpy(b)) if diff else None
+    got = N.state_norms(ad, bd)
+    again = N.state_norms(ad, bd)
+    torch.cuda.synchronize()
+    ref = oracle.planner.state_norm(a, b)
+    np.testing.assert_allclose(got.cpu().double().numpy(), ref, rtol=NORM_RTOL, atol=0)
+    assert torch.equal(got, again), "not deterministic"
+
+
+def planner_inputs(P, seed):
+    g = np.random.default_rng(seed)
+    norms = g.uniform(0.1, 3.0, P).astype(np.float32)
+    w = g.dirichlet(np.ones(P)).astype(np.float32)
+    drift = np.float32(g.uniform(0.01, 0.5))
+    return norms, w, drift
+
+
+@pytest.mark.parametrize("P,local,group", [(32, 16, 4), (11, 4, 3), (8, 0, 8), (5, 4, 2), (256, 100, 16),
+                                           (7, 3, 10), (1, 0, 1)])
+def test_planner_decide_matches_oracle(P, local, group):
+    norms, w, drift = planner_inputs(P, P + 1000 * local + group)
+    note(f"planner decide P={P} local={local} group={group}")
+    ase_ref = oracle.planner.planner(norms, drift, w, local, group, 0.0, 0.2)["ase"]
+    for eps in (-np.inf, 0.0, float(np.median(ase_ref)), 1e9):
+        eps32 = np.float32(eps)
+        r = N.planner_decide(to_dev(torch.from_numpy(norms)), to_dev(torch.tensor([drift])),
+                             to_dev(torch.from_numpy(w)), to_dev(torch.tensor([eps32])), local, group, 0.2)
+        torch.cuda.synchronize()
+        ref = oracle.planner.planner(norms, drift, w, local, group, float(eps32), 0.2)
+        for key in ("alpha", "delta", "ase"):
+            np.testing.assert_allclose(r[key].cpu().double().numpy(), ref[key], rtol=PLAN_RTOL, atol=0)
+        # the decision is an integer taken on the GPU's own fp32 errors: the oracle takes it on the same numbers
+        gpu_ase = r["ase"].cpu().double().numpy()
+        assert np.array_equal(r["compute"].cpu().numpy(), oracle.planner.decide(gpu_ase, local, group, float(eps32)))
+        assert int(r["anchor"].item()) == int(ref["anchor"])
+    # the anchor flag on both sides of eps_local
+    r = N.planner_decide(to_dev(torch.from_numpy(norms)), to_dev(torch.tensor([drift])), to_dev(torch.from_numpy(w)),
+                         to_dev(torch.tensor([0.0])), local, group, float(drift) * 2)
+    assert int(r["anchor"].item()) == 0
+
+
+@pytest.mark.parametrize("P,local,group", [(32, 16, 4), (11, 4, 3), (256, 7, 2), (8, 0, 8), (5, 4, 1)])
+def test_planner_epsilon_matches_oracle(P, local, group):
+    g = np.random.default_rng(P * 31 + local + group)
+    corr = g.uniform(0.0, 1.0, P).astype(np.float32)
+    w = g.dirichlet(np.ones(P)).astype(np.float32)
+    note(f"planner epsilon P={P} local={local} group={group}")
+    for R in (0.0, 0.1, 1 / 3, 0.5, 0.75, 1.0):
+        eps = N.planner_epsilon(to_dev(torch.from_numpy(corr)), to_dev(torch.from_numpy(w)), local, group, R)
+        torch.cuda.synchronize()
+        got = float(eps.item())
+        ref = oracle.planner.epsilon(corr, w, local, group, R)
+        if np.isinf(ref):
+            assert got == -np.inf, (R, got)
+        else:
+            assert abs(got - ref) <= PLAN_RTOL * abs(ref), (R, got, ref)
+
+
+# --------------------------------------------------------------------------- #
 # Full-size workloads, sampled rows
 # --------------------------------------------------------------------------- #
 
@@ -294,3 +369,26 @@ def test_full_size_long_video_and_selective_reuse(reuse_workload):
     note(f"selective reuse: MSE vs full attention {mse:.3e}; near weight {mean_w[w.near].sum():.3f}")
     assert mean_w[w.near].sum() > 0.5
     assert mse < 1e-2
+    # planner statistics at full size, against the oracle applied to the GPU's own states
+    eps = to_dev(torch.tensor([1e-4], dtype=torch.float32))
+    runner.plan_anchor()
+    plan = runner.plan_step(w.local, 4, eps, 0.5)
+    torch.cuda.synchronize()
+    n_ref = np.array([oracle.planner.state_norm(runner.state_out[i].view(1, -1).cpu().numpy())[0]
+                      for i in range(w.P)])
+    np.testing.assert_allclose(runner.anchor_norms.cpu().double().numpy(), n_ref, rtol=NORM_RTOL, atol=0)
+    fresh = runner.step_out[runner.near.index(w.local)].view(1, -1).cpu().numpy()
+    d_ref = oracle.planner.state_norm(fresh, runner.state_out[w.local].view(1, -1).cpu().numpy())[0]
+    np.testing.assert_allclose(runner.local_drift.cpu().double().numpy(), [d_ref], rtol=NORM_RTOL, atol=0)
+    _, gw_ref = oracle.contribution(runner.state_lse.reshape(w.P, -1).cpu().numpy(), runner.rows)
+    assert np.abs(runner.global_weights.cpu().double().numpy() - gw_ref).max() <= F32_TOL
+    ref = oracle.planner.planner(runner.anchor_norms.cpu().numpy(), float(runner.local_drift.item()),
+                                 runner.global_weights.view(-1).cpu().numpy(), w.local, 4, 1e-4, 0.5)
+    np.testing.assert_allclose(plan["ase"].cpu().double().numpy(), ref["ase"], rtol=PLAN_RTOL, atol=0)
+    gpu_ase = plan["ase"].cpu().double().numpy()
+    assert np.array_equal(plan["compute"].cpu().numpy(),
+                          oracle.planner.decide(gpu_ase, w.local, 4, float(np.float32(1e-4))))
+    alpha = plan["alpha"].cpu().numpy()
+    note(f"planner: local drift {runner.local_drift.item():.4g}, alpha near/far "
+         f"{alpha[w.near].mean():.3f}/{np.delete(alpha, w.near).mean():.3f}, "
+         f"group errors {np.array2string(gpu_ase, precision=2)}, compute {plan['compute'].cpu().numpy().tolist()}")
