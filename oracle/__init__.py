@@ -11,6 +11,7 @@ against library routines, closed forms, invariants and a hand-worked example
 (``tests/golden/``). No function is "parity unpinned".
 """
 from .states import (  # noqa: F401
+    compose_groups,
     contribution,
     full_attention,
     merge,

@@ -16,6 +16,10 @@ Sources (page titles as on the pages; no line numbers):
   importance w(i, t) is the softmax of the LSE values over partitions.
 * Same page, "Core claim" and Fig. 6 caption: fresh states for high-contribution
   partitions, cached composed states for the others.
+* Same page, "If this is right": a state is about half the size of the KV it
+  summarises, and composed states can be merged into coarser groups under memory
+  pressure (group-wise composition; group size g of 4, 8 or 16 in the
+  free-parameter ledger).
 
 Readings where the page is silent:
 
@@ -124,6 +128,18 @@ def merge(outs, lses) -> Tuple[np.ndarray, np.ndarray]:
 def merge_pair(a: Tuple[np.ndarray, np.ndarray], b: Tuple[np.ndarray, np.ndarray]):
     """Composition of two states; the k = 2 case of ``merge``."""
     return merge(np.stack([_f64(a[0]), _f64(b[0])]), np.stack([_f64(a[1]), _f64(b[1])]))
+
+
+def compose_groups(outs, lses, group: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Group-wise composition: the states of partitions k*group .. (k+1)*group - 1 (the
+    last group may be shorter) merged into one state per group.
+
+    outs [P, ..., D], lses [P, ...] -> [G, ..., D], [G, ...] with G = ceil(P / group).
+    """
+    outs, lses = _f64(outs), _f64(lses)
+    P = outs.shape[0]
+    parts = [merge(outs[k:k + group], lses[k:k + group]) for k in range(0, P, group)]
+    return np.stack([o for o, _ in parts]), np.stack([l for _, l in parts])
 
 
 def contribution(lse, rows_per_group: int) -> Tuple[np.ndarray, np.ndarray]:

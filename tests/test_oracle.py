@@ -229,6 +229,33 @@ def check_reuse(orc):
     assert errs[0] < 1e-25 < errs[1] < errs[2]
 
 
+def check_compose_groups(orc):
+    g = np.random.default_rng(21)
+    P, rows, D = 7, 5, 3
+    outs = g.standard_normal((P, rows, D))
+    lses = g.standard_normal((P, rows)) * 4
+    outs[5], lses[5] = 0.0, -np.inf            # one empty partition
+    full_o, full_l = orc.merge(outs, lses)
+    # groups of one: the states themselves, bit for bit
+    o1, l1 = orc.compose_groups(outs, lses, 1)
+    assert np.array_equal(o1, outs) and np.array_equal(l1, lses)
+    for group in (2, 3, 4, 7, 9):
+        go, gl = orc.compose_groups(outs, lses, group)
+        assert go.shape == ((P + group - 1) // group, rows, D)
+        # composing the group states again gives the composition of all of them
+        mo, ml = orc.merge(go, gl)
+        np.testing.assert_allclose(mo, full_o, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(ml, full_l, rtol=0, atol=1e-12)
+        # the last group holds exactly the last partitions
+        k = (P - 1) // group
+        lo, ll = orc.merge(outs[k * group:], lses[k * group:])
+        np.testing.assert_allclose(go[-1], lo, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(gl[-1], ll, rtol=0, atol=1e-12)
+    # a group made only of empty states is the empty state
+    e_o, e_l = orc.compose_groups(np.zeros((2, rows, D)), np.full((2, rows), -np.inf), 2)
+    assert np.all(e_o == 0) and np.all(np.isneginf(e_l))
+
+
 # --------------------------------------------------------------------------- #
 # Planner statistics (Eqs. 9, 10, 12, 13, Algorithm 1)
 # --------------------------------------------------------------------------- #
@@ -336,7 +363,7 @@ def check_epsilon(orc):
 
 PINS = [check_golden, check_bruteforce_loops, check_states_vs_sdpa, check_merge_equals_full,
         check_identity_bitexact, check_closed_forms, check_contribution, check_reuse,
-        check_planner_golden, check_norms, check_planner_invariants, check_epsilon]
+        check_compose_groups, check_planner_golden, check_norms, check_planner_invariants, check_epsilon]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -410,6 +437,9 @@ MUTANTS = {
     "reuse caches the new step": ("c_out, c_lse = merge(out_t[far], lse_t[far])",
                                   "c_out, c_lse = merge(_f64(out_t1)[far], _f64(lse_t1)[far])"),
     "range end off by one": ("k[b, h, s:e], v[b, h, s:e]", "k[b, h, s:e + 1], v[b, h, s:e + 1]"),
+    "group overlaps the next one": ("merge(outs[k:k + group], lses[k:k + group])",
+                                    "merge(outs[k:k + group + 1], lses[k:k + group + 1])"),
+    "groups skip a partition": ("for k in range(0, P, group)]", "for k in range(0, P, group + 1)]"),
     # planner.py
     "alpha inverted": ("return n / n[local]", "return n[local] / n", "planner.py"),
     "drift not scaled by alpha": ("return _f64(alpha) * float(local_drift)",
