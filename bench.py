@@ -263,6 +263,46 @@ def main():
             if by:
                 kernels[name].update({"GB/s": round(by / ms / 1e6, 1), "frac_hbm": round(by / ms / 1e6 / PEAK_HBM_GBPS, 4)})
 
+        # compact (bf16 OUT) states, timed on their own: the anchor writing bf16 states, the
+        # 28-way composition of the far ones, and group-wise composition of all 32 (g = 4)
+        st16 = torch.empty(runner.state_out.shape, dtype=torch.bfloat16, device=dev)
+        c16 = torch.empty(runner.state_out.shape[1:], dtype=torch.bfloat16, device=dev)
+        c16_lse = torch.empty(runner.state_lse.shape[1:], dtype=torch.float32, device=dev)
+        G = (w.P + 3) // 4
+        g16 = torch.empty((G,) + tuple(runner.state_out.shape[1:]), dtype=torch.bfloat16, device=dev)
+        g16_lse = torch.empty((G,) + tuple(runner.state_lse.shape[1:]), dtype=torch.float32, device=dev)
+        far = runner.far
+
+        def compact_calls():
+            runner._timed("attn_anchor_bf16_states", N.partition_attn_states, q, k, v, w.ranges, w.scale,
+                          torch.bfloat16, out=st16, lse=runner.state_lse)
+            runner._timed("merge_cached_bf16", N.merge_states, [st16[i] for i in far],
+                          [runner.state_lse[i] for i in far], torch.bfloat16, out=c16, lse=c16_lse)
+            runner._timed("compose_groups_g4_bf16", N.compose_groups, st16, runner.state_lse, 4, torch.bfloat16,
+                          out=g16, lse=g16_lse)
+
+        runner.timer = None
+        compact_calls()
+        torch.cuda.synchronize()
+        runner.timer = []
+        for _ in range(max(1, args.steps // 2)):
+            compact_calls()
+        torch.cuda.synchronize()
+        ctimes = {}
+        for name, s, e in runner.timer:
+            ctimes.setdefault(name, []).append(s.elapsed_time(e))
+        st16_bytes = rows * (2 * w.D + 4)
+        ms = sum(ctimes["attn_anchor_bf16_states"]) / len(ctimes["attn_anchor_bf16_states"])
+        kernels["attn_anchor_bf16_states"] = {"ms": round(ms, 4), "TFLOP/s": round(attn_flops["attn_anchor"] / ms / 1e9, 1)}
+        for name, by in (("merge_cached_bf16", (len(far) + 1) * st16_bytes),
+                         ("compose_groups_g4_bf16", (w.P + G) * st16_bytes)):
+            ms = sum(ctimes[name]) / len(ctimes[name])
+            kernels[name] = {"ms": round(ms, 4), "GB/s": round(by / ms / 1e6, 1),
+                             "frac_hbm": round(by / ms / 1e6 / PEAK_HBM_GBPS, 4)}
+        kernels["state_bytes_per_row"] = {"fp32": 4 * w.D + 4, "bf16": 2 * w.D + 4,
+                                          "kv_bytes_per_key_bf16": 4 * w.D}
+        del st16, c16, g16
+
     traffic = measured_traffic()
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,

@@ -105,6 +105,55 @@ as_status as_merge(int32_t n, const float* const* outs, const float* const* lses
                    int64_t rows, int64_t D, float* out, float* lse, hipStream_t stream);
 
 /*
+ * Compact states and group-wise composition.
+ *   Source: DiTango review page (pith.science), "If this is right": an attention
+ *   state is about half the size of the KV it summarises, and composed states can
+ *   be merged into coarser groups under memory pressure; the free-parameter ledger
+ *   gives the group size g (4, 8 or 16 explored).
+ * A state's OUT may be stored as float32 (AS_F32) or bfloat16 (AS_BF16, rounded to
+ * nearest even); LSE is always float32. A bf16 state of D = 128 takes 2D + 4 = 260
+ * bytes per query row against 516 for fp32. All arithmetic is fp32 either way.
+ */
+
+/*
+ * as_partition_attn_states - as_partition_attn with the OUT storage type chosen
+ * by state_dtype (AS_F32 gives exactly as_partition_attn). out is DEVICE
+ * [P][B][H][Sq][D] of state_dtype, contiguous, 16-byte aligned; every other
+ * argument and rule is as for as_partition_attn.
+ */
+as_status as_partition_attn_states(const void* q, const void* k, const void* v, as_dtype dtype,
+                                   int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
+                                   const int64_t q_stride[3], const int64_t kv_stride[3],
+                                   const int32_t* kv_ranges, int32_t P, float scale, as_dtype state_dtype,
+                                   void* out, float* lse, hipStream_t stream);
+
+/*
+ * as_merge_states - as_merge for states whose OUT is stored as in_dtype, writing an
+ * OUT of out_dtype (AS_F32/AS_F32 gives exactly as_merge). outs: HOST array of n
+ * DEVICE pointers, each [rows][D] of in_dtype; out: DEVICE [rows][D] of out_dtype.
+ * OUT pointers are 16-byte aligned for fp32 and 8-byte aligned for bf16 (a slice of
+ * a bf16 block with D a multiple of 4 always is). Other rules as for as_merge.
+ */
+as_status as_merge_states(int32_t n, const void* const* outs, const float* const* lses, as_dtype in_dtype,
+                          int64_t rows, int64_t D, as_dtype out_dtype, void* out, float* lse, hipStream_t stream);
+
+/*
+ * as_compose_groups - group-wise composition: the states of partitions
+ * k*group .. min((k+1)*group, P) - 1 of a partition-major block are composed (as in
+ * as_merge) into one state per group k, for all G = ceil(P / group) groups in one
+ * launch.
+ *
+ * outs, lses  DEVICE [P][rows][D] of in_dtype (16-byte aligned) and float32 [P][rows]
+ *             (as written by as_partition_attn_states).
+ * P           1 <= P <= AS_MAX_PARTITIONS.   group: 1 <= group <= AS_MAX_MERGE.
+ * rows, D     rows >= 0; D a multiple of 4, 4 <= D <= 1024.
+ * out, lse    DEVICE [G][rows][D] of out_dtype (16-byte aligned) and float32 [G][rows];
+ *             must not overlap the input blocks.
+ */
+as_status as_compose_groups(const void* outs, const float* lses, as_dtype in_dtype, int32_t P, int64_t rows,
+                            int64_t D, int32_t group, as_dtype out_dtype, void* out, float* lse, hipStream_t stream);
+
+/*
  * as_partition_contribution_workspace_size - bytes of device workspace that
  * as_partition_contribution needs to compute scores for these sizes (per-chunk
  * partial sums of the group reduction). Returns 0 for invalid sizes.

@@ -21,7 +21,8 @@ AS_BF16, AS_F32 = 0, 1
 AS_MAX_PARTITIONS = 256
 AS_MAX_MERGE = 64
 
-EXPORTS = ("as_partition_attn", "as_merge", "as_partition_contribution_workspace_size",
+EXPORTS = ("as_partition_attn", "as_merge", "as_partition_attn_states", "as_merge_states", "as_compose_groups",
+           "as_partition_contribution_workspace_size",
            "as_partition_contribution", "as_state_norms_workspace_size", "as_state_norms",
            "as_planner_decide", "as_planner_epsilon", "as_status_string", "as_last_error")
 
@@ -61,6 +62,16 @@ def lib() -> ctypes.CDLL:
         L.as_merge.restype = ctypes.c_int
         L.as_merge.argtypes = [ctypes.c_int32, c_vpp, c_vpp, ctypes.c_int64, ctypes.c_int64,
                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.as_partition_attn_states.restype = ctypes.c_int
+        L.as_partition_attn_states.argtypes = L.as_partition_attn.argtypes[:14] + [ctypes.c_int, ctypes.c_void_p,
+                                                                                   ctypes.c_void_p, ctypes.c_void_p]
+        L.as_merge_states.restype = ctypes.c_int
+        L.as_merge_states.argtypes = [ctypes.c_int32, c_vpp, c_vpp, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.as_compose_groups.restype = ctypes.c_int
+        L.as_compose_groups.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int32, ctypes.c_int64,
+                                        ctypes.c_int64, ctypes.c_int32, ctypes.c_int, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p]
         L.as_partition_contribution_workspace_size.restype = ctypes.c_size_t
         L.as_partition_contribution_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int64]
         L.as_partition_contribution.restype = ctypes.c_int
@@ -111,6 +122,15 @@ def _i64(vals) -> ctypes.Array:
 # as_partition_attn
 # --------------------------------------------------------------------------- #
 
+_STATE_DTYPES = {torch.float32: AS_F32, torch.bfloat16: AS_BF16}
+
+
+def _state_code(dtype: torch.dtype) -> int:
+    if dtype not in _STATE_DTYPES:
+        raise ValueError("state OUT must be float32 or bfloat16")
+    return _STATE_DTYPES[dtype]
+
+
 def partition_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_ranges: Sequence[Tuple[int, int]],
                    scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
                    lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
@@ -118,6 +138,18 @@ def partition_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_ranges:
 
     Returns OUT [P,B,H,Sq,D] and LSE [P,B,H,Sq] (float32), enqueued on the current stream.
     """
+    return _attn(q, k, v, kv_ranges, scale, out, lse, None)
+
+
+def partition_attn_states(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_ranges: Sequence[Tuple[int, int]],
+                          scale: Optional[float] = None, state_dtype: torch.dtype = torch.bfloat16,
+                          out: Optional[torch.Tensor] = None,
+                          lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """As partition_attn, with OUT stored as state_dtype (float32 or bfloat16); LSE is float32."""
+    return _attn(q, k, v, kv_ranges, scale, out, lse, state_dtype)
+
+
+def _attn(q, k, v, kv_ranges, scale, out, lse, state_dtype):
     _require_gpu(q, k, v)
     if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or k.stride() != v.stride():
         raise ValueError("q must be [B,H,Sq,D]; k and v [B,H,Skv,D] with equal strides")
@@ -130,21 +162,26 @@ def partition_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_ranges:
         raise ValueError("the head dimension must be contiguous")
     Skv = k.shape[2]
     P = len(kv_ranges)
+    odt = torch.float32 if state_dtype is None else state_dtype
+    code = _state_code(odt)
     if out is None:
-        out = torch.empty((P, B, H, Sq, D), dtype=torch.float32, device=q.device)
+        out = torch.empty((P, B, H, Sq, D), dtype=odt, device=q.device)
     if lse is None:
         lse = torch.empty((P, B, H, Sq), dtype=torch.float32, device=q.device)
-    if not (out.is_contiguous() and lse.is_contiguous() and out.dtype == torch.float32 and lse.dtype == torch.float32):
-        raise ValueError("out and lse must be contiguous float32")
+    if not (out.is_contiguous() and lse.is_contiguous() and out.dtype == odt and lse.dtype == torch.float32):
+        raise ValueError("out must be contiguous of the state dtype and lse contiguous float32")
     if out.numel() != P * B * H * Sq * D or lse.numel() != P * B * H * Sq:
         raise ValueError("out/lse have the wrong size")
     flat = [int(x) for r in kv_ranges for x in r]
     ranges = (ctypes.c_int32 * max(1, len(flat)))(*flat)
     dt = AS_BF16 if q.dtype == torch.bfloat16 else AS_F32
     sc = float(D ** -0.5 if scale is None else scale)
-    check(lib().as_partition_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), dt, B, H, Sq, Skv, D,
-                                  _i64(q.stride()[:3]), _i64(k.stride()[:3]), ranges, P, sc,
-                                  out.data_ptr(), lse.data_ptr(), _stream(q)))
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), dt, B, H, Sq, Skv, D,
+            _i64(q.stride()[:3]), _i64(k.stride()[:3]), ranges, P, sc)
+    if state_dtype is None:
+        check(lib().as_partition_attn(*args, out.data_ptr(), lse.data_ptr(), _stream(q)))
+    else:
+        check(lib().as_partition_attn_states(*args, code, out.data_ptr(), lse.data_ptr(), _stream(q)))
     return out, lse
 
 
@@ -173,6 +210,57 @@ def merge(outs: Sequence[torch.Tensor], lses: Sequence[torch.Tensor], out: Optio
     optrs = (ctypes.c_void_p * n)(*[o.data_ptr() for o in outs])
     lptrs = (ctypes.c_void_p * n)(*[l.data_ptr() for l in lses])
     check(lib().as_merge(n, optrs, lptrs, rows, D, out.data_ptr(), lse.data_ptr(), _stream(outs[0])))
+    return out, lse
+
+
+def merge_states(outs: Sequence[torch.Tensor], lses: Sequence[torch.Tensor], out_dtype: torch.dtype = torch.bfloat16,
+                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """Compose n states whose OUT is float32 or bfloat16 (all the same); OUT written as out_dtype."""
+    n = len(outs)
+    if n != len(lses) or n == 0:
+        raise ValueError("need the same positive number of OUT and LSE tensors")
+    _require_gpu(*outs, *lses)
+    in_dtype = outs[0].dtype
+    in_code, out_code = _state_code(in_dtype), _state_code(out_dtype)
+    D = outs[0].shape[-1]
+    rows = outs[0].numel() // D
+    for o, l in zip(outs, lses):
+        if o.dtype != in_dtype or l.dtype != torch.float32 or not o.is_contiguous() or not l.is_contiguous():
+            raise ValueError("states must be contiguous, OUT of one dtype, LSE float32")
+        if o.numel() != rows * D or l.numel() != rows:
+            raise ValueError("states disagree in size")
+    if out is None:
+        out = torch.empty(outs[0].shape, dtype=out_dtype, device=outs[0].device)
+    if lse is None:
+        lse = torch.empty(lses[0].shape, dtype=torch.float32, device=outs[0].device)
+    optrs = (ctypes.c_void_p * n)(*[o.data_ptr() for o in outs])
+    lptrs = (ctypes.c_void_p * n)(*[l.data_ptr() for l in lses])
+    check(lib().as_merge_states(n, optrs, lptrs, in_code, rows, D, out_code, out.data_ptr(), lse.data_ptr(),
+                                _stream(outs[0])))
+    return out, lse
+
+
+def compose_groups(outs: torch.Tensor, lses: torch.Tensor, group: int, out_dtype: Optional[torch.dtype] = None,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """Group-wise composition of a partition-major block of states OUT [P, ..., D], LSE [P, ...]:
+    one state per group of `group` consecutive partitions ([G, ..., D], [G, ...])."""
+    _require_gpu(outs, lses)
+    if not outs.is_contiguous() or not lses.is_contiguous() or lses.dtype != torch.float32:
+        raise ValueError("states must be contiguous with float32 LSE")
+    in_code = _state_code(outs.dtype)
+    out_dtype = outs.dtype if out_dtype is None else out_dtype
+    out_code = _state_code(out_dtype)
+    P, D = outs.shape[0], outs.shape[-1]
+    rows = outs.numel() // max(P * D, 1)
+    if lses.shape[0] != P or lses.numel() != P * rows:
+        raise ValueError("OUT and LSE blocks disagree")
+    G = (P + group - 1) // max(group, 1)
+    if out is None:
+        out = torch.empty((G,) + tuple(outs.shape[1:]), dtype=out_dtype, device=outs.device)
+    if lse is None:
+        lse = torch.empty((G,) + tuple(lses.shape[1:]), dtype=torch.float32, device=outs.device)
+    check(lib().as_compose_groups(outs.data_ptr(), lses.data_ptr(), in_code, P, rows, D, group, out_code,
+                                  out.data_ptr(), lse.data_ptr(), _stream(outs)))
     return out, lse
 
 

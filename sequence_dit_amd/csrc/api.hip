@@ -49,12 +49,16 @@ const char* as_status_string(as_status s) {
 
 const char* as_last_error(void) { return g_last_error; }
 
-as_status as_partition_attn(const void* q, const void* k, const void* v, as_dtype dtype,
-                            int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
-                            const int64_t q_stride[3], const int64_t kv_stride[3],
-                            const int32_t* kv_ranges, int32_t P, float scale,
-                            float* out, float* lse, hipStream_t stream) {
+namespace {
+
+as_status attn_impl(const void* q, const void* k, const void* v, as_dtype dtype,
+                    int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
+                    const int64_t q_stride[3], const int64_t kv_stride[3],
+                    const int32_t* kv_ranges, int32_t P, float scale, as_dtype state_dtype,
+                    void* out, float* lse, hipStream_t stream) {
   if (dtype != AS_BF16 && dtype != AS_F32) return fail(AS_ERR_INVALID_ARG, "dtype %d is not AS_BF16 or AS_F32", (int)dtype);
+  if (state_dtype != AS_BF16 && state_dtype != AS_F32)
+    return fail(AS_ERR_INVALID_ARG, "state_dtype %d is not AS_BF16 or AS_F32", (int)state_dtype);
   if (B < 0 || H < 0 || Sq < 0 || Skv < 0) return fail(AS_ERR_INVALID_ARG, "negative size (B=%lld H=%lld Sq=%lld Skv=%lld)",
                                                        (long long)B, (long long)H, (long long)Sq, (long long)Skv);
   if (D < 1) return fail(AS_ERR_INVALID_ARG, "D=%lld must be positive", (long long)D);
@@ -98,6 +102,7 @@ as_status as_partition_attn(const void* q, const void* k, const void* v, as_dtyp
   a.q_sb = q_stride[0]; a.q_sh = q_stride[1]; a.q_ss = q_stride[2];
   a.k_sb = kv_stride[0]; a.k_sh = kv_stride[1]; a.k_ss = kv_stride[2];
   a.out = out; a.lse = lse;
+  a.out_bf16 = state_dtype == AS_BF16 ? 1 : 0;
   a.B = (int32_t)B; a.H = (int32_t)H; a.Sq = (int32_t)Sq; a.Skv = (int32_t)Skv; a.D = (int32_t)D; a.P = P;
   a.scale = scale;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
@@ -115,26 +120,103 @@ as_status as_partition_attn(const void* q, const void* k, const void* v, as_dtyp
   return hip_status(as::launch_attn_f32(a, stream), "partition_attn f32 launch");
 }
 
-as_status as_merge(int32_t n, const float* const* outs, const float* const* lses,
-                   int64_t rows, int64_t D, float* out, float* lse, hipStream_t stream) {
+bool is_state_dtype(as_dtype t) { return t == AS_F32 || t == AS_BF16; }
+
+as_status merge_impl(int32_t n, const void* const* outs, const float* const* lses, as_dtype in_dtype,
+                     int64_t rows, int64_t D, as_dtype out_dtype, void* out, float* lse, hipStream_t stream) {
+  if (!is_state_dtype(in_dtype) || !is_state_dtype(out_dtype))
+    return fail(AS_ERR_INVALID_ARG, "state dtypes must be AS_F32 or AS_BF16");
   if (n < 1 || n > AS_MAX_MERGE) return fail(AS_ERR_INVALID_ARG, "n=%d outside [1, %d]", n, AS_MAX_MERGE);
   if (rows < 0) return fail(AS_ERR_INVALID_ARG, "rows=%lld is negative", (long long)rows);
   if (D < 4 || D > 1024 || D % 4) return fail(AS_ERR_INVALID_ARG, "D=%lld must be a multiple of 4 in [4, 1024]", (long long)D);
   if (!outs || !lses) return fail(AS_ERR_INVALID_ARG, "NULL pointer list");
   if (rows == 0) return ok();
   if (!out || !lse) return fail(AS_ERR_INVALID_ARG, "NULL output pointer");
-  if (!aligned(out, 16) || !aligned(lse, 4)) return fail(AS_ERR_INVALID_ARG, "out must be 16-byte and lse 4-byte aligned");
+  // OUT is read and written 4 elements at a time: 16 bytes of fp32, 8 of bf16
+  const size_t ain = in_dtype == AS_BF16 ? 8 : 16, aout = out_dtype == AS_BF16 ? 8 : 16;
+  if (!aligned(out, aout) || !aligned(lse, 4))
+    return fail(AS_ERR_INVALID_ARG, "out must be %zu-byte and lse 4-byte aligned", aout);
   as::MergeArgs a;
   memset(&a, 0, sizeof(a));
   for (int32_t i = 0; i < n; ++i) {
     if (!outs[i] || !lses[i]) return fail(AS_ERR_INVALID_ARG, "input %d has a NULL pointer", i);
-    if (!aligned(outs[i], 16) || !aligned(lses[i], 4)) return fail(AS_ERR_INVALID_ARG, "input %d is misaligned", i);
+    if (!aligned(outs[i], ain) || !aligned(lses[i], 4)) return fail(AS_ERR_INVALID_ARG, "input %d is misaligned", i);
     if (outs[i] == out || lses[i] == lse) return fail(AS_ERR_INVALID_ARG, "input %d aliases the output", i);
     a.outs[i] = outs[i];
     a.lses[i] = lses[i];
   }
   a.out = out; a.lse = lse; a.rows = rows; a.n = n; a.D = (int32_t)D;
+  a.in_bf16 = in_dtype == AS_BF16; a.out_bf16 = out_dtype == AS_BF16;
+  a.vec2 = D % 8 == 0 && aligned(out, 16);
+  for (int32_t i = 0; i < n; ++i) a.vec2 = a.vec2 && aligned(outs[i], 16);
   return hip_status(as::launch_merge(a, stream), "merge launch");
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+as_status as_partition_attn(const void* q, const void* k, const void* v, as_dtype dtype,
+                            int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
+                            const int64_t q_stride[3], const int64_t kv_stride[3],
+                            const int32_t* kv_ranges, int32_t P, float scale,
+                            float* out, float* lse, hipStream_t stream) {
+  return attn_impl(q, k, v, dtype, B, H, Sq, Skv, D, q_stride, kv_stride, kv_ranges, P, scale, AS_F32, out, lse,
+                   stream);
+}
+
+as_status as_partition_attn_states(const void* q, const void* k, const void* v, as_dtype dtype,
+                                   int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
+                                   const int64_t q_stride[3], const int64_t kv_stride[3],
+                                   const int32_t* kv_ranges, int32_t P, float scale, as_dtype state_dtype,
+                                   void* out, float* lse, hipStream_t stream) {
+  return attn_impl(q, k, v, dtype, B, H, Sq, Skv, D, q_stride, kv_stride, kv_ranges, P, scale, state_dtype, out, lse,
+                   stream);
+}
+
+as_status as_merge_states(int32_t n, const void* const* outs, const float* const* lses, as_dtype in_dtype,
+                          int64_t rows, int64_t D, as_dtype out_dtype, void* out, float* lse, hipStream_t stream) {
+  return merge_impl(n, outs, lses, in_dtype, rows, D, out_dtype, out, lse, stream);
+}
+
+as_status as_compose_groups(const void* outs, const float* lses, as_dtype in_dtype, int32_t P, int64_t rows,
+                            int64_t D, int32_t group, as_dtype out_dtype, void* out, float* lse, hipStream_t stream) {
+  if (!is_state_dtype(in_dtype) || !is_state_dtype(out_dtype))
+    return fail(AS_ERR_INVALID_ARG, "state dtypes must be AS_F32 or AS_BF16");
+  if (P < 1 || P > AS_MAX_PARTITIONS) return fail(AS_ERR_INVALID_ARG, "P=%d outside [1, %d]", P, AS_MAX_PARTITIONS);
+  if (group < 1 || group > AS_MAX_MERGE) return fail(AS_ERR_INVALID_ARG, "group=%d outside [1, %d]", group, AS_MAX_MERGE);
+  if (rows < 0) return fail(AS_ERR_INVALID_ARG, "rows=%lld is negative", (long long)rows);
+  if (D < 4 || D > 1024 || D % 4) return fail(AS_ERR_INVALID_ARG, "D=%lld must be a multiple of 4 in [4, 1024]", (long long)D);
+  if (rows == 0) return ok();
+  if (!outs || !lses || !out || !lse) return fail(AS_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned(outs, 16) || !aligned(out, 16) || !aligned(lses, 4) || !aligned(lse, 4))
+    return fail(AS_ERR_INVALID_ARG, "OUT blocks must be 16-byte and LSE blocks 4-byte aligned");
+  const int64_t G = (P + group - 1) / group;
+  const size_t ein = in_dtype == AS_BF16 ? 2 : 4, eout = out_dtype == AS_BF16 ? 2 : 4;
+  if (overlap(outs, (size_t)(P * rows * D) * ein, out, (size_t)(G * rows * D) * eout) ||
+      overlap(lses, (size_t)(P * rows) * 4, lse, (size_t)(G * rows) * 4) ||
+      overlap(outs, (size_t)(P * rows * D) * ein, lse, (size_t)(G * rows) * 4) ||
+      overlap(lses, (size_t)(P * rows) * 4, out, (size_t)(G * rows * D) * eout))
+    return fail(AS_ERR_INVALID_ARG, "outputs overlap the input blocks");
+  as::MergeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.base_out = outs; a.base_lse = lses; a.out = out; a.lse = lse;
+  a.rows = rows; a.n = P; a.D = (int32_t)D; a.group = group;
+  a.in_bf16 = in_dtype == AS_BF16; a.out_bf16 = out_dtype == AS_BF16;
+  a.vec2 = D % 8 == 0;   // slices of rows*D elements keep 16-byte alignment when D % 8 == 0
+  return hip_status(as::launch_merge(a, stream), "compose_groups launch");
+}
+
+as_status as_merge(int32_t n, const float* const* outs, const float* const* lses,
+                   int64_t rows, int64_t D, float* out, float* lse, hipStream_t stream) {
+  const void* ptrs[AS_MAX_MERGE];
+  if (n >= 1 && n <= AS_MAX_MERGE && outs)
+    for (int32_t i = 0; i < n; ++i) ptrs[i] = outs[i];
+  return merge_impl(n, (n >= 1 && n <= AS_MAX_MERGE && outs) ? ptrs : nullptr, lses, AS_F32, rows, D, AS_F32, out, lse,
+                    stream);
 }
 
 size_t as_partition_contribution_workspace_size(int32_t P, int64_t rows, int64_t rows_per_group) {

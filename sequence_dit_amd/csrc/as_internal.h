@@ -17,23 +17,34 @@ struct AttnArgs {
   const void* v;
   int64_t q_sb, q_sh, q_ss;  // element strides of q over (b, h, s)
   int64_t k_sb, k_sh, k_ss;  // element strides of k and v over (b, h, s)
-  float* out;                // [P][B][H][Sq][D]
+  void* out;                 // [P][B][H][Sq][D], float or bf16 (out_bf16)
   float* lse;                // [P][B][H][Sq]
   int32_t B, H, Sq, Skv, D, P;
   int32_t n_qtiles;          // ceil(Sq / rows per workgroup)
   float scale;               // softmax scale
   float scale_log2;          // scale * log2(e)
+  int32_t out_bf16;          // OUT stored as bf16 (rounded to nearest even) instead of float
   int32_t ranges[2 * AS_MAX_PARTITIONS];
 };
 
+// k-way composition. Pointer mode (group == 0): inputs outs[k], lses[k], k < n.
+// Batched mode (group > 0, group-wise composition): n = P slices of one
+// partition-major block (base_out [P][rows][D], base_lse [P][rows]); grid.y = group
+// index k, whose inputs are slices k*group .. min((k+1)*group, P) - 1; outputs are
+// [G][rows][D] and [G][rows].
 struct MergeArgs {
-  const float* outs[AS_MAX_MERGE];
+  const void* outs[AS_MAX_MERGE];   // float or bf16 [rows][D] each
   const float* lses[AS_MAX_MERGE];
-  float* out;
+  const void* base_out;
+  const float* base_lse;
+  void* out;                        // float or bf16
   float* lse;
   int64_t rows;
   int32_t n;
   int32_t D;
+  int32_t group;
+  int32_t in_bf16, out_bf16;
+  int32_t vec2;   // bf16 inputs: every OUT pointer 16-byte aligned and D % 8 == 0 (16-byte lane loads)
 };
 
 struct ContribArgs {

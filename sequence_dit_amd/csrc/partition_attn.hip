@@ -40,6 +40,24 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// Stores of OUT elements: fp32, or bf16 rounded to nearest even.
+template <bool BF16>
+__device__ __forceinline__ void store_out4(void* base, int64_t off, f32x4 v) {
+  if (BF16) {
+    const bf16x4 h = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+    *reinterpret_cast<u32x2*>(static_cast<__bf16*>(base) + off) = __builtin_bit_cast(u32x2, h);
+  } else {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(base) + off) = v;
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_out1(void* base, int64_t off, float v) {
+  if (BF16) static_cast<__bf16*>(base)[off] = (__bf16)v;
+  else static_cast<float*>(base)[off] = v;
+}
 
 constexpr int kWaves = 8;
 constexpr int kQB = 1;                       // 32-row query blocks per wave
@@ -310,7 +328,7 @@ struct Stager {
 // stages K (tile t+2 during Y_t), group 0 stages V (tile t during Y_t); two LDS
 // slots per operand suffice for this offset: a slot is rewritten only after both
 // groups' last read of its previous tile.
-template <int D>
+template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_kernel(const AttnArgs a) {
   using L = Lds<D>;
@@ -338,7 +356,6 @@ void attn_bf16_kernel(const AttnArgs a) {
   const int n = ke - ks;
   const int q0 = qtile * kBQ;
   const int64_t row_base = ((int64_t)part * a.B * a.H + bh) * a.Sq;   // row index in out/lse
-  float* __restrict__ out = a.out + row_base * D;
   float* __restrict__ lse = a.lse + row_base;
 
   if (n <= 0) {  // empty partition: the identity state (0, -inf)
@@ -346,8 +363,7 @@ void attn_bf16_kernel(const AttnArgs a) {
       const int q = q0 + r;
       if (q < a.Sq) {
         lse[q] = -INFINITY;
-        f32x4* o4 = reinterpret_cast<f32x4*>(out + (int64_t)q * D);
-        for (int c = 0; c < D / 4; ++c) o4[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < D / 4; ++c) store_out4<OUT_BF16>(a.out, (row_base + q) * D + 4 * c, f32x4{0.f, 0.f, 0.f, 0.f});
       }
     }
     return;
@@ -480,14 +496,14 @@ void attn_bf16_kernel(const AttnArgs a) {
   const float lt = wave_sum_halves(w.l);
   const float inv = 1.0f / lt;
   if (qrow < a.Sq) {
-    float* orow = out + (int64_t)qrow * D;
+    const int64_t orow = (row_base + qrow) * D;
 #pragma unroll
     for (int db = 0; db < W::NDB; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const f32x4 val = {w.o[db][4 * j] * inv, w.o[db][4 * j + 1] * inv, w.o[db][4 * j + 2] * inv,
                            w.o[db][4 * j + 3] * inv};
-        *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * j + 4 * half) = val;
+        store_out4<OUT_BF16>(a.out, orow + db * 32 + 8 * j + 4 * half, val);
       }
     if (half == 0) lse[qrow] = (w.m + __log2f(lt)) * 0.69314718055994530942f;
   }
@@ -503,7 +519,7 @@ constexpr int kF32Rows = 64;
 constexpr int kF32Threads = 256;
 constexpr int kF32Keys = 32;
 
-template <int DC>  // D / 4 elements per lane (1..32)
+template <int DC, bool OUT_BF16>  // D / 4 elements per lane (1..32)
 __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(const AttnArgs a) {
   const int D = a.D;
   __shared__ float ks_[kF32Keys][128 + 4];
@@ -519,7 +535,6 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(const AttnArgs a)
   const int ksb = a.ranges[2 * part], keb = a.ranges[2 * part + 1];
   const int n = keb - ksb;
   const int64_t row_base = ((int64_t)part * a.B * a.H + bh) * a.Sq;
-  float* out = a.out + row_base * D;
   float* lse = a.lse + row_base;
   const int dc = D / 4;   // elements per lane
 
@@ -575,11 +590,11 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(const AttnArgs a)
   }
   if (q < a.Sq) {
     if (n <= 0) {
-      for (int e = 0; e < dc; ++e) out[(int64_t)q * D + sub * dc + e] = 0.f;
+      for (int e = 0; e < dc; ++e) store_out1<OUT_BF16>(a.out, (row_base + q) * D + sub * dc + e, 0.f);
       if (sub == 0) lse[q] = -INFINITY;
     } else {
       for (int e = 0; e < DC; ++e)
-        if (e < dc) out[(int64_t)q * D + sub * dc + e] = acc[e] / l;
+        if (e < dc) store_out1<OUT_BF16>(a.out, (row_base + q) * D + sub * dc + e, acc[e] / l);
       if (sub == 0) lse[q] = m + logf(l);
     }
   }
@@ -596,9 +611,11 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream) {
   if (total > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)total), block(kThreads);
   if (a.D == 128) {
-    hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, block, 0, stream, a);
+    if (a.out_bf16) hipLaunchKernelGGL((attn_bf16_kernel<128, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_bf16_kernel<128, false>), grid, block, 0, stream, a);
   } else if (a.D == 64) {
-    hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, block, 0, stream, a);
+    if (a.out_bf16) hipLaunchKernelGGL((attn_bf16_kernel<64, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_bf16_kernel<64, false>), grid, block, 0, stream, a);
   } else {
     return hipErrorInvalidValue;
   }
@@ -612,11 +629,14 @@ hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)((a.Sq + kF32Rows - 1) / kF32Rows), (unsigned)gy), block(kF32Threads);
   const int dc = a.D / 4;
   if (dc <= 8) {
-    hipLaunchKernelGGL(attn_f32_kernel<8>, grid, block, 0, stream, a);
+    if (a.out_bf16) hipLaunchKernelGGL((attn_f32_kernel<8, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_f32_kernel<8, false>), grid, block, 0, stream, a);
   } else if (dc <= 16) {
-    hipLaunchKernelGGL(attn_f32_kernel<16>, grid, block, 0, stream, a);
+    if (a.out_bf16) hipLaunchKernelGGL((attn_f32_kernel<16, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_f32_kernel<16, false>), grid, block, 0, stream, a);
   } else if (dc <= 32) {
-    hipLaunchKernelGGL(attn_f32_kernel<32>, grid, block, 0, stream, a);
+    if (a.out_bf16) hipLaunchKernelGGL((attn_f32_kernel<32, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_f32_kernel<32, false>), grid, block, 0, stream, a);
   } else {
     return hipErrorInvalidValue;
   }

@@ -254,3 +254,66 @@ def test_planner_bindings_refuse_cpu_tensors():
         N.state_norms(x)
     with pytest.raises(ValueError, match="HIP device"):
         N.planner_epsilon(x[0], x[1], 0, 2, 0.5)
+
+
+def test_partition_attn_states_rejects_bad_state_dtype():
+    args = dict(q=FAKE, k=FAKE, v=FAKE, dtype=N.AS_BF16, B=1, H=2, Sq=16, Skv=64, D=128)
+    flat = [0, 32, 32, 64]
+    rng = (ctypes.c_int32 * 4)(*flat)
+    st = N.lib().as_partition_attn_states(FAKE, FAKE, FAKE, N.AS_BF16, 1, 2, 16, 64, 128, N._i64((4096, 2048, 128)),
+                                          N._i64((16384, 8192, 128)), rng, 2, 0.088, 7, FAKE, FAKE, None)
+    assert st == N.AS_ERR_INVALID_ARG and "state_dtype" in N.lib().as_last_error().decode()
+
+
+def merge_states_call(n=2, in_dt=N.AS_BF16, out_dt=N.AS_F32, rows=10, D=128, out=FAKE, lse=FAKE, ptrs=None):
+    ptrs = ptrs if ptrs is not None else [FAKE + 0x1000 * (i + 1) for i in range(max(n, 1))]
+    optrs = (ctypes.c_void_p * len(ptrs))(*ptrs)
+    lptrs = (ctypes.c_void_p * len(ptrs))(*ptrs)
+    st = N.lib().as_merge_states(n, optrs, lptrs, in_dt, rows, D, out_dt, out, lse, None)
+    return st, N.lib().as_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(in_dt=5), N.AS_ERR_INVALID_ARG, "state dtypes"),
+    (dict(out_dt=-1), N.AS_ERR_INVALID_ARG, "state dtypes"),
+    (dict(n=0), N.AS_ERR_INVALID_ARG, "n=0"),
+    (dict(n=65, ptrs=[FAKE] * 65), N.AS_ERR_INVALID_ARG, "n=65"),
+    (dict(D=6), N.AS_ERR_INVALID_ARG, "multiple of 4"),
+    (dict(out=FAKE + 8), N.AS_ERR_INVALID_ARG, "16-byte"),
+    (dict(ptrs=[FAKE + 4, FAKE + 0x2000]), N.AS_ERR_INVALID_ARG, "misaligned"),
+    (dict(in_dt=N.AS_F32, ptrs=[FAKE + 8, FAKE + 0x2000]), N.AS_ERR_INVALID_ARG, "misaligned"),
+    (dict(ptrs=[FAKE, FAKE + 0x1000], out=FAKE), N.AS_ERR_INVALID_ARG, "aliases"),
+])
+def test_merge_states_rejects(kw, status, text):
+    st, msg = merge_states_call(**kw)
+    assert st == status, msg
+    assert text in msg
+
+
+def compose_call(outs=FAKE, lses=FAKE + 0x100000, in_dt=N.AS_F32, P=8, rows=16, D=128, group=4,
+                 out_dt=N.AS_F32, out=FAKE + 0x200000, lse=FAKE + 0x300000):
+    st = N.lib().as_compose_groups(outs, lses, in_dt, P, rows, D, group, out_dt, out, lse, None)
+    return st, N.lib().as_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(in_dt=9), N.AS_ERR_INVALID_ARG, "state dtypes"),
+    (dict(P=0), N.AS_ERR_INVALID_ARG, "P=0"),
+    (dict(P=257), N.AS_ERR_INVALID_ARG, "P=257"),
+    (dict(group=0), N.AS_ERR_INVALID_ARG, "group=0"),
+    (dict(group=65), N.AS_ERR_INVALID_ARG, "group=65"),
+    (dict(rows=-1), N.AS_ERR_INVALID_ARG, "negative"),
+    (dict(D=2), N.AS_ERR_INVALID_ARG, "multiple of 4"),
+    (dict(outs=0), N.AS_ERR_INVALID_ARG, "NULL"),
+    (dict(out=FAKE + 0x200008), N.AS_ERR_INVALID_ARG, "aligned"),
+    (dict(out=FAKE + 0x1000), N.AS_ERR_INVALID_ARG, "overlap"),      # inside the 8 x 16 x 128 x 4 B input block
+    (dict(lse=FAKE + 0x100010), N.AS_ERR_INVALID_ARG, "overlap"),   # inside the LSE block
+])
+def test_compose_groups_rejects(kw, status, text):
+    st, msg = compose_call(**kw)
+    assert st == status, msg
+    assert text in msg
+
+
+def test_compose_groups_zero_rows_ok_without_gpu():
+    assert compose_call(rows=0)[0] == N.AS_OK

@@ -177,6 +177,111 @@ def test_merge_with_empty_state_is_bitwise_identity():
     assert torch.all(m_out == 0) and torch.all(torch.isneginf(m_lse))
 
 
+# --------------------------------------------------------------------------- #
+# Compact (bf16 OUT) states and group-wise composition
+# --------------------------------------------------------------------------- #
+
+def bf16_close(got, ref, what):
+    """Within one bf16 rounding of the reference (2^-8 relative) plus fp32 noise."""
+    err = np.abs(got - ref) - (np.abs(ref) * 2.0 ** -8 + 1e-6)
+    assert np.all(err <= 0), f"{what}: off by more than a bf16 rounding (worst excess {err.max():.3e})"
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_bf16_states_are_rounded_fp32_states(D):
+    w = inputs.small_case(11 + D, 1, 3, 300, 1000, D, RAGGED)
+    note(f"bf16 states D={D}")
+    q, k, v = to_dev(w.q), to_dev(w.k), to_dev(w.v)
+    o32, l32 = N.partition_attn(q, k, v, w.ranges, w.scale)
+    o16, l16 = N.partition_attn_states(q, k, v, w.ranges, w.scale, torch.bfloat16)
+    torch.cuda.synchronize()
+    # the same arithmetic, then one round-to-nearest-even of OUT
+    assert o16.dtype == torch.bfloat16 and torch.equal(o16, o32.to(torch.bfloat16))
+    assert torch.equal(l16, l32)
+    o_ref, l_ref = oracle.partition_states(w.q, w.k, w.v, w.ranges, w.scale)
+    check_states(o16.float(), l16, o_ref, l_ref, BF16_OUT, BF16_LSE, f"bf16 states D={D}")
+
+
+def test_f32_inputs_with_bf16_states():
+    w = inputs.small_case(12, 1, 2, 70, 300, 40, [(0, 100), (100, 300), (50, 51), (7, 7)], dtype=torch.float32)
+    note("f32 inputs, bf16 states")
+    q, k, v = to_dev(w.q), to_dev(w.k), to_dev(w.v)
+    o32, l32 = N.partition_attn(q, k, v, w.ranges, w.scale)
+    o16, l16 = N.partition_attn_states(q, k, v, w.ranges, w.scale, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o16, o32.to(torch.bfloat16)) and torch.equal(l16, l32)
+    o_ref, l_ref = oracle.partition_states(w.q, w.k, w.v, w.ranges, w.scale)
+    fin = np.isfinite(l_ref)
+    bf16_close(o16.float().cpu().double().numpy()[fin], o_ref[fin], "f32 inputs, bf16 OUT")
+    assert np.abs(l16.cpu().double().numpy()[fin] - l_ref[fin]).max() <= F32_TOL
+
+
+@pytest.mark.parametrize("n,rows,D,in_dt,out_dt", [
+    (28, 300, 128, torch.bfloat16, torch.bfloat16), (5, 777, 128, torch.bfloat16, torch.float32),
+    (4, 129, 64, torch.float32, torch.bfloat16), (64, 33, 4, torch.bfloat16, torch.bfloat16),
+    (9, 301, 40, torch.bfloat16, torch.float32), (3, 50, 1024, torch.float32, torch.float32)])
+def test_merge_states_matches_oracle(n, rows, D, in_dt, out_dt):
+    outs, lses = random_states(n * 7 + D, n, rows, D, n_empty=rows // 3)
+    outs[:, 0] = 0
+    lses[:, 0] = -np.inf
+    note(f"merge_states n={n} rows={rows} D={D} {in_dt}->{out_dt}")
+    od = to_dev(torch.from_numpy(outs)).to(in_dt)
+    ld = to_dev(torch.from_numpy(lses))
+    m_out, m_lse = N.merge_states(list(od), list(ld), out_dt)
+    torch.cuda.synchronize()
+    # the oracle composes exactly the stored inputs
+    r_out, r_lse = oracle.merge(od.float().cpu().numpy(), lses)
+    got = m_out.float().cpu().double().numpy()
+    if out_dt == torch.float32:
+        check_states(m_out, m_lse, r_out, r_lse, F32_TOL, F32_TOL, "merge_states")
+    else:
+        bf16_close(got, r_out, "merge_states bf16 OUT")
+        fin = np.isfinite(r_lse)
+        assert np.abs(m_lse.cpu().double().numpy()[fin] - r_lse[fin]).max() <= F32_TOL
+        assert np.all(np.isneginf(m_lse.cpu().numpy()[~fin])) and np.all(got[~fin] == 0)
+    if in_dt == torch.float32 and out_dt == torch.float32:
+        f_out, f_lse = N.merge(list(od), list(ld))
+        assert torch.equal(f_out, m_out) and torch.equal(f_lse, m_lse)
+
+
+def test_merge_states_bf16_identity():
+    outs, lses = random_states(6, 1, 257, 128)
+    x = to_dev(torch.from_numpy(outs[0])).to(torch.bfloat16)
+    xl = to_dev(torch.from_numpy(lses[0]))
+    e, el = torch.zeros_like(x), torch.full_like(xl, float("-inf"))
+    m_out, m_lse = N.merge_states([e, x, e], [el, xl, el], torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(m_out.view(torch.int16), x.view(torch.int16)) and torch.equal(m_lse, xl)
+
+
+@pytest.mark.parametrize("P,group,rows,D,in_dt,out_dt", [
+    (32, 4, 300, 128, torch.bfloat16, torch.bfloat16), (7, 3, 129, 64, torch.float32, torch.float32),
+    (32, 8, 3840, 128, torch.float32, torch.bfloat16), (5, 64, 33, 4, torch.bfloat16, torch.float32),
+    (256, 16, 20, 128, torch.bfloat16, torch.bfloat16), (6, 1, 50, 32, torch.float32, torch.float32)])
+def test_compose_groups_matches_oracle(P, group, rows, D, in_dt, out_dt):
+    outs, lses = random_states(P * 3 + group, P, rows, D, n_empty=rows // 2)
+    outs[:, 1] = 0
+    lses[:, 1] = -np.inf
+    note(f"compose_groups P={P} group={group} rows={rows} D={D} {in_dt}->{out_dt}")
+    od = to_dev(torch.from_numpy(outs)).to(in_dt)
+    ld = to_dev(torch.from_numpy(lses))
+    g_out, g_lse = N.compose_groups(od, ld, group, out_dt)
+    torch.cuda.synchronize()
+    r_out, r_lse = oracle.compose_groups(od.float().cpu().numpy(), lses, group)
+    assert g_out.shape[0] == (P + group - 1) // group
+    if out_dt == torch.float32:
+        check_states(g_out, g_lse, r_out, r_lse, F32_TOL, F32_TOL, "compose_groups")
+    else:
+        bf16_close(g_out.float().cpu().double().numpy(), r_out, "compose_groups bf16 OUT")
+        fin = np.isfinite(r_lse)
+        assert np.abs(g_lse.cpu().double().numpy()[fin] - r_lse[fin]).max() <= F32_TOL
+    # one launch over all groups gives, bit for bit, the per-group merges
+    for k in range(0, P, max(1, P // 4 // group) * group):
+        m_out, m_lse = N.merge_states(list(od[k:k + group]), list(ld[k:k + group]), out_dt)
+        torch.cuda.synchronize()
+        assert torch.equal(m_out, g_out[k // group]) and torch.equal(m_lse, g_lse[k // group]), k
+
+
 def test_merge_tree_equals_flat_on_gpu():
     """Associativity and commutativity on the device: ((a,b),(c,(d,e))) equals the flat 5-way merge."""
     outs, lses = random_states(77, 5, 400, 128)
