@@ -22,3 +22,4 @@ from .states import (  # noqa: F401
     selective_reuse,
 )
 from . import planner  # noqa: F401  (anchor-guided planner statistics)
+from . import fp8  # noqa: F401  (E4M3 codes -> values for the fp8-input path)

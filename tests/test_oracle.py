@@ -361,9 +361,56 @@ def check_epsilon(orc):
     assert pl.epsilon(corr, w, local, group, 0.0) == -math.inf
 
 
+FP8_HAND = {  # E4M3 codes worked by hand: sign | exponent (bias 7) | mantissa
+    0x00: 0.0, 0x38: 1.0, 0xB8: -1.0, 0x39: 1.125, 0x40: 2.0, 0x30: 0.5, 0x77: 240.0, 0x7E: 448.0,
+    0xFE: -448.0, 0x08: 2.0 ** -6, 0x07: 7 / 8 * 2.0 ** -6, 0x01: 2.0 ** -9, 0x81: -(2.0 ** -9)}
+
+
+def check_fp8(orc):
+    """E4M3 decoding: hand-worked codes, the NaN codes, torch's own float8_e4m3fn
+    conversion on all 256 codes (library routine), strict monotonicity of the
+    positive codes, and per-(b, h) dequantisation on a brute-force loop."""
+    dec = orc.fp8.decode_e4m3
+    for c, v in FP8_HAND.items():
+        assert dec(np.array([c]))[0] == v, (hex(c), dec(np.array([c]))[0], v)
+    assert np.isnan(dec(np.array([0x7F, 0xFF]))).all()
+    codes = np.arange(256, dtype=np.uint8)
+    mine = dec(codes)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok])
+    assert np.all(np.diff(mine[:127]) > 0)
+    g = np.random.default_rng(5)
+    cq = g.integers(0, 256, size=(2, 3, 4, 5)).astype(np.uint8)
+    cq[cq & 0x7F == 0x7F] = 0x38
+    sc = np.array([[0.5, 2.0, 3.0], [1.0, 0.25, 7.0]])
+    got = orc.fp8.dequantize(cq, sc)
+    for b in range(2):
+        for h in range(3):
+            for i in range(4):
+                for j in range(5):
+                    assert got[b, h, i, j] == FP8_ALL[int(cq[b, h, i, j])] * sc[b, h]
+
+
+def _fp8_table():
+    """Every finite E4M3 value by enumeration of (sign, exponent, mantissa) fields."""
+    t = {}
+    for c in range(256):
+        sgn, e, m = c >> 7, (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            continue
+        mag = (m / 8) * 2.0 ** -6 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+        t[c] = -mag if sgn else mag
+    return t
+
+
+FP8_ALL = _fp8_table()
+
+
 PINS = [check_golden, check_bruteforce_loops, check_states_vs_sdpa, check_merge_equals_full,
         check_identity_bitexact, check_closed_forms, check_contribution, check_reuse,
-        check_compose_groups, check_planner_golden, check_norms, check_planner_invariants, check_epsilon]
+        check_compose_groups, check_planner_golden, check_norms, check_planner_invariants, check_epsilon, check_fp8]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -422,6 +469,11 @@ def test_smooth_component_gives_spatial_locality():
 # --------------------------------------------------------------------------- #
 
 MUTANTS = {
+    "fp8 exponent bias off by one": ("BIAS = 7", "BIAS = 8", "fp8.py"),
+    "fp8 subnormal exponent": ("np.exp2(1.0 - BIAS)", "np.exp2(-BIAS)", "fp8.py"),
+    "fp8 mantissa width": ("(1.0 + m / 8.0)", "(1.0 + m / 16.0)", "fp8.py"),
+    "fp8 sign bit": ("np.where(c & 0x80, -1.0, 1.0)", "np.where(c & 0x40, -1.0, 1.0)", "fp8.py"),
+    "fp8 scale of the wrong head": ("vals * s[:, :, None, None]", "vals * s[:, ::-1, None, None]", "fp8.py"),
     # states.py
     "scale dropped": ("z = scale * (q @ k.T)", "z = (q @ k.T)"),
     "keys used as values": ("return p @ v, lse", "return p @ k, lse"),
@@ -467,11 +519,12 @@ def mutant_module(old, new, file="states.py"):
     mod = types.ModuleType("oracle_mutant_" + file[:-3])
     mod.__file__ = src_path
     exec(compile(src.replace(old, new), src_path, "exec"), mod.__dict__)
-    if file == "planner.py":
+    if file in ("planner.py", "fp8.py"):
         pkg = types.SimpleNamespace(**{k: getattr(oracle, k) for k in dir(oracle) if not k.startswith("_")})
-        pkg.planner = mod
+        setattr(pkg, file[:-3], mod)
         return pkg
     mod.planner = oracle.planner
+    mod.fp8 = oracle.fp8
     return mod
 
 
