@@ -128,6 +128,37 @@ as_status as_partition_attn_states(const void* q, const void* k, const void* v, 
                                    void* out, float* lse, hipStream_t stream);
 
 /*
+ * as_partition_attn_fp8 - as_partition_attn_states with 8-bit floating-point
+ * queries and keys.
+ *   Sources: the DiTango review page (pith.science) cites SageAttention, 8-bit
+ *   attention for plug-and-play inference, among its references; the FastUSP page
+ *   (mlsanity) quantises attention traffic to FP8 and builds on "FP8 Formats for
+ *   Deep Learning", which defines the E4M3 format used here.
+ * q and k hold FP8 E4M3 codes, one byte per element, in the OCP "e4m3fn" encoding
+ * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no infinities; largest
+ * finite value 448; torch.float8_e4m3fn). v is bfloat16. A code c of batch b and
+ * head h stands for the value c * q_scale[b*H + h] in q and c * k_scale[b*H + h] in
+ * k, so the states are those of as_partition_attn on the dequantised Q and K and
+ * the given V:  z_j = scale * < q_scale[bh] * Q8_r , k_scale[bh] * K8_j >.
+ * S = K Q^T runs on the fp8 MFMA (exact products, fp32 accumulation); softmax, P and
+ * PV are as in the bf16 path.
+ *
+ * q_scale, k_scale  DEVICE float32 [B*H], 4-byte aligned; values must be finite and
+ *                   positive (not checked: they are device memory).
+ * q_stride          element (= byte) strides of q over (b, h, s).
+ * kv_stride         element strides of k and v over (b, h, s): k's row stride is
+ *                   kv_stride[2] bytes, v's 2 * kv_stride[2] bytes. All strides are
+ *                   multiples of 16 elements.
+ * D                 64 or 128 (else AS_ERR_UNSUPPORTED).
+ * Every other argument and rule is as for as_partition_attn_states.
+ */
+as_status as_partition_attn_fp8(const void* q, const void* k, const void* v, const float* q_scale,
+                                const float* k_scale, int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
+                                const int64_t q_stride[3], const int64_t kv_stride[3],
+                                const int32_t* kv_ranges, int32_t P, float scale, as_dtype state_dtype,
+                                void* out, float* lse, hipStream_t stream);
+
+/*
  * as_merge_states - as_merge for states whose OUT is stored as in_dtype, writing an
  * OUT of out_dtype (AS_F32/AS_F32 gives exactly as_merge). outs: HOST array of n
  * DEVICE pointers, each [rows][D] of in_dtype; out: DEVICE [rows][D] of out_dtype.

@@ -21,7 +21,8 @@ AS_BF16, AS_F32 = 0, 1
 AS_MAX_PARTITIONS = 256
 AS_MAX_MERGE = 64
 
-EXPORTS = ("as_partition_attn", "as_merge", "as_partition_attn_states", "as_merge_states", "as_compose_groups",
+EXPORTS = ("as_partition_attn", "as_merge", "as_partition_attn_states", "as_partition_attn_fp8",
+           "as_merge_states", "as_compose_groups",
            "as_partition_contribution_workspace_size",
            "as_partition_contribution", "as_state_norms_workspace_size", "as_state_norms",
            "as_planner_decide", "as_planner_epsilon", "as_status_string", "as_last_error")
@@ -65,6 +66,12 @@ def lib() -> ctypes.CDLL:
         L.as_partition_attn_states.restype = ctypes.c_int
         L.as_partition_attn_states.argtypes = L.as_partition_attn.argtypes[:14] + [ctypes.c_int, ctypes.c_void_p,
                                                                                    ctypes.c_void_p, ctypes.c_void_p]
+        L.as_partition_attn_fp8.restype = ctypes.c_int
+        L.as_partition_attn_fp8.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                            ctypes.c_int64, ctypes.c_int64, c_i64p, c_i64p, c_i32p, ctypes.c_int32,
+                                            ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p]
         L.as_merge_states.restype = ctypes.c_int
         L.as_merge_states.argtypes = [ctypes.c_int32, c_vpp, c_vpp, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
                                       ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
@@ -147,6 +154,49 @@ def partition_attn_states(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_
                           lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """As partition_attn, with OUT stored as state_dtype (float32 or bfloat16); LSE is float32."""
     return _attn(q, k, v, kv_ranges, scale, out, lse, state_dtype)
+
+
+def partition_attn_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_scale: torch.Tensor,
+                       k_scale: torch.Tensor, kv_ranges: Sequence[Tuple[int, int]], scale: Optional[float] = None,
+                       state_dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None,
+                       lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Attention states from fp8 E4M3 queries and keys (torch.float8_e4m3fn, [B,H,Sq,D] and
+    [B,H,Skv,D]) with float32 dequantisation factors q_scale, k_scale [B,H] (a code c of
+    (b, h) stands for c * scale[b, h]) and bfloat16 values v (same shape and strides as k).
+    Returns OUT [P,B,H,Sq,D] of state_dtype and LSE [P,B,H,Sq] float32."""
+    _require_gpu(q, k, v, q_scale, k_scale)
+    fp8 = torch.float8_e4m3fn
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or k.stride() != v.stride():
+        raise ValueError("q must be [B,H,Sq,D]; k and v [B,H,Skv,D] with equal strides")
+    if q.dtype != fp8 or k.dtype != fp8 or v.dtype != torch.bfloat16:
+        raise ValueError("q and k must be float8_e4m3fn and v bfloat16")
+    B, H, Sq, D = q.shape
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != D:
+        raise ValueError("q and k/v disagree on B, H or D")
+    if q.stride(3) != 1 or k.stride(3) != 1:
+        raise ValueError("the head dimension must be contiguous")
+    for t in (q_scale, k_scale):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != B * H:
+            raise ValueError("q_scale and k_scale must be contiguous float32 [B, H]")
+    Skv = k.shape[2]
+    P = len(kv_ranges)
+    code = _state_code(state_dtype)
+    if out is None:
+        out = torch.empty((P, B, H, Sq, D), dtype=state_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((P, B, H, Sq), dtype=torch.float32, device=q.device)
+    if not (out.is_contiguous() and lse.is_contiguous() and out.dtype == state_dtype and lse.dtype == torch.float32):
+        raise ValueError("out must be contiguous of the state dtype and lse contiguous float32")
+    if out.numel() != P * B * H * Sq * D or lse.numel() != P * B * H * Sq:
+        raise ValueError("out/lse have the wrong size")
+    flat = [int(x) for r in kv_ranges for x in r]
+    ranges = (ctypes.c_int32 * max(1, len(flat)))(*flat)
+    sc = float(D ** -0.5 if scale is None else scale)
+    check(lib().as_partition_attn_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_scale.data_ptr(),
+                                      k_scale.data_ptr(), B, H, Sq, Skv, D, _i64(q.stride()[:3]),
+                                      _i64(k.stride()[:3]), ranges, P, sc, code, out.data_ptr(), lse.data_ptr(),
+                                      _stream(q)))
+    return out, lse
 
 
 def _attn(q, k, v, kv_ranges, scale, out, lse, state_dtype):

@@ -55,7 +55,8 @@ as_status attn_impl(const void* q, const void* k, const void* v, as_dtype dtype,
                     int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
                     const int64_t q_stride[3], const int64_t kv_stride[3],
                     const int32_t* kv_ranges, int32_t P, float scale, as_dtype state_dtype,
-                    void* out, float* lse, hipStream_t stream) {
+                    void* out, float* lse, hipStream_t stream,
+                    bool qk_fp8 = false, const float* q_scale = nullptr, const float* k_scale = nullptr) {
   if (dtype != AS_BF16 && dtype != AS_F32) return fail(AS_ERR_INVALID_ARG, "dtype %d is not AS_BF16 or AS_F32", (int)dtype);
   if (state_dtype != AS_BF16 && state_dtype != AS_F32)
     return fail(AS_ERR_INVALID_ARG, "state_dtype %d is not AS_BF16 or AS_F32", (int)state_dtype);
@@ -72,15 +73,19 @@ as_status attn_impl(const void* q, const void* k, const void* v, as_dtype dtype,
                   i, (long long)s, (long long)e, (long long)Skv);
   }
   if (dtype == AS_BF16 && D != 64 && D != 128)
-    return fail(AS_ERR_UNSUPPORTED, "bf16 path supports D in {64, 128}, got %lld", (long long)D);
+    return fail(AS_ERR_UNSUPPORTED, "%s path supports D in {64, 128}, got %lld", qk_fp8 ? "fp8" : "bf16", (long long)D);
   if (dtype == AS_F32 && (D % 4 != 0 || D > 128))
     return fail(AS_ERR_UNSUPPORTED, "f32 path supports D a multiple of 4 up to 128, got %lld", (long long)D);
   const int64_t rows = B * H * Sq;
   if (rows == 0 || P == 0) return ok();
   if (!q || !k || !v || !out || !lse) return fail(AS_ERR_INVALID_ARG, "NULL tensor pointer");
   if (!q_stride || !kv_stride) return fail(AS_ERR_INVALID_ARG, "NULL stride array");
-  const int64_t esz = dtype == AS_BF16 ? 2 : 4;
-  const int64_t smul = dtype == AS_BF16 ? 8 : 4;
+  if (qk_fp8 && (!q_scale || !k_scale)) return fail(AS_ERR_INVALID_ARG, "q_scale and k_scale must not be NULL");
+  if (qk_fp8 && (!aligned(q_scale, 4) || !aligned(k_scale, 4)))
+    return fail(AS_ERR_INVALID_ARG, "q_scale and k_scale must be 4-byte aligned");
+  const int64_t esz = dtype == AS_BF16 ? 2 : 4;   // bytes per v element (the widest input)
+  // fp8 rows are read 16 bytes at a time: 16 one-byte elements
+  const int64_t smul = qk_fp8 ? 16 : dtype == AS_BF16 ? 8 : 4;
   for (int j = 0; j < 3; ++j) {
     if (q_stride[j] < 0 || kv_stride[j] < 0) return fail(AS_ERR_INVALID_ARG, "negative stride");
     if (q_stride[j] % smul || kv_stride[j] % smul)
@@ -103,6 +108,9 @@ as_status attn_impl(const void* q, const void* k, const void* v, as_dtype dtype,
   a.k_sb = kv_stride[0]; a.k_sh = kv_stride[1]; a.k_ss = kv_stride[2];
   a.out = out; a.lse = lse;
   a.out_bf16 = state_dtype == AS_BF16 ? 1 : 0;
+  a.qk_fp8 = qk_fp8 ? 1 : 0;
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
   a.B = (int32_t)B; a.H = (int32_t)H; a.Sq = (int32_t)Sq; a.Skv = (int32_t)Skv; a.D = (int32_t)D; a.P = P;
   a.scale = scale;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
@@ -175,6 +183,15 @@ as_status as_partition_attn_states(const void* q, const void* k, const void* v, 
                                    void* out, float* lse, hipStream_t stream) {
   return attn_impl(q, k, v, dtype, B, H, Sq, Skv, D, q_stride, kv_stride, kv_ranges, P, scale, state_dtype, out, lse,
                    stream);
+}
+
+as_status as_partition_attn_fp8(const void* q, const void* k, const void* v, const float* q_scale,
+                                const float* k_scale, int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
+                                const int64_t q_stride[3], const int64_t kv_stride[3],
+                                const int32_t* kv_ranges, int32_t P, float scale, as_dtype state_dtype,
+                                void* out, float* lse, hipStream_t stream) {
+  return attn_impl(q, k, v, AS_BF16, B, H, Sq, Skv, D, q_stride, kv_stride, kv_ranges, P, scale, state_dtype, out, lse,
+                   stream, true, q_scale, k_scale);
 }
 
 as_status as_merge_states(int32_t n, const void* const* outs, const float* const* lses, as_dtype in_dtype,

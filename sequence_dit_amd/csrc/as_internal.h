@@ -24,6 +24,9 @@ struct AttnArgs {
   float scale;               // softmax scale
   float scale_log2;          // scale * log2(e)
   int32_t out_bf16;          // OUT stored as bf16 (rounded to nearest even) instead of float
+  int32_t qk_fp8;            // q and k are fp8 e4m3 (v stays bf16), dequantised by q_scale, k_scale
+  const float* q_scale;      // [B*H] (qk_fp8 only)
+  const float* k_scale;      // [B*H] (qk_fp8 only)
   int32_t ranges[2 * AS_MAX_PARTITIONS];
 };
 

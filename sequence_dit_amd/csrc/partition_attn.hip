@@ -30,6 +30,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "as_internal.h"
 
 namespace as {
@@ -41,6 +43,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // Stores of OUT elements: fp32, or bf16 rounded to nearest even.
 template <bool BF16>
@@ -102,13 +105,46 @@ __device__ __forceinline__ void lds_barrier() {
 constexpr int kLookahead = 6;
 
 
+// Compile-time loop: f(integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Step plan of an fp8 MFMA phase: NS S steps (two 16-byte operand units each) and
+// NPV PV steps (one unit each); one S step precedes every R PV steps.
+template <int NS_, int NPV_>
+struct Fp8Plan {
+  static constexpr int NS = NS_, NPV = NPV_, N = NS + NPV, NU = 2 * NS + NPV;
+  static constexpr int R = (NS > 0 && NPV > 0) ? NPV / NS : 0;
+  static_assert(NS == 0 || NPV == 0 || NPV % NS == 0, "step interleave");
+  static constexpr int LA = NU < kLookahead ? NU : kLookahead;
+  static constexpr bool is_s(int j) { return NS == 0 ? false : NPV == 0 ? true : j % (R + 1) == 0; }
+  static constexpr int idx(int j) {
+    return (NS == 0 || NPV == 0) ? j : (j % (R + 1) == 0 ? j / (R + 1) : j - j / (R + 1) - 1);
+  }
+  static constexpr int ustart(int j) {
+    int u = 0;
+    for (int i = 0; i < j; ++i) u += is_s(i) ? 2 : 1;
+    return u;
+  }
+  static constexpr int unit_step(int u) {
+    int j = 0;
+    while (ustart(j + 1) <= u) ++j;
+    return j;
+  }
+};
+
 // LDS layout of one workgroup (bytes). Rows are padded by 16 bytes instead of
 // XOR-swizzled, so every operand address is a per-lane base plus a compile-time
 // immediate. K tiles are [key][d]; V tiles are transposed, [d][key], with the keys
 // of a row permuted so that the 8 keys one lane feeds to an MFMA are contiguous.
-template <int D>
+template <int D, bool QK8>
 struct Lds {
-  static constexpr int KP = D * 2 + 16;        // K row pitch
+  static constexpr int KP = D * (QK8 ? 1 : 2) + 16;   // K row pitch (fp8 or bf16 keys)
   static constexpr int KTILE = kBK * KP;
   static constexpr int VP = kBK * 2 + 16;      // V^T row pitch
   static constexpr int VTILE = D * VP;
@@ -123,12 +159,18 @@ __device__ __forceinline__ constexpr int vt_group_pos(int g) {
   return 16 * (((g >> 2) << 1) | (g & 1)) + 8 * ((g >> 1) & 1);
 }
 
+// Q fragments (B operand of S^T) of one lane. bf16: Q[row l32][d = 16ds + 8half .. +7].
+// fp8: Q[row l32][d = 64ds + 32half .. +31]; the fp8 MFMA pairs byte j of a lane half
+// of A with byte j of the same lane half of B, so K and Q only need the same d order.
+template <int D, bool QK8> struct QFrag { bf16x8 v[D / 16]; };
+template <int D> struct QFrag<D, true> { i32x8 v[D / 64]; };
+
 // Per-wave state of the bf16 kernel; one wave owns 32 query rows.
-template <int D>
+template <int D, bool QK8>
 struct Wave {
-  static constexpr int NDS = D / 16;   // MFMA k-steps of S^T = K Q^T
-  static constexpr int NDB = D / 32;   // 32-wide d blocks of O^T
-  bf16x8 qf[NDS];        // Q (B operand of S^T): Q[row l32][d = 16ds + 8half .. +7]
+  static constexpr int NDS = QK8 ? D / 64 : D / 16;   // MFMA k-steps of S^T = K Q^T
+  static constexpr int NDB = D / 32;                  // 32-wide d blocks of O^T
+  QFrag<D, QK8> qf;      // Q, for the whole partition
   f32x16 s[2];           // S^T of the current tile: [kb], reg r <-> key 32kb + 8(r/4) + 4half + r%4
   bf16x8 pf[2][2];       // P of the previous tile, B operand of O^T: [kb][c]
   f32x16 o[NDB];         // O^T: [db], reg r <-> d = 32db + 8(r/4) + 4half + r%4
@@ -143,7 +185,13 @@ struct Wave {
   // the wave drains the LDS queue).
   template <int KS, int VS, bool DO_S, bool DO_PV>
   __device__ __forceinline__ void mfma_phase(const char* smem) {
-    using L = Lds<D>;
+    if constexpr (QK8) mfma_phase_fp8<KS, VS, DO_S, DO_PV>(smem);
+    else mfma_phase_bf16<KS, VS, DO_S, DO_PV>(smem);
+  }
+
+  template <int KS, int VS, bool DO_S, bool DO_PV>
+  __device__ __forceinline__ void mfma_phase_bf16(const char* smem) {
+    using L = Lds<D, QK8>;
     constexpr int NS = DO_S ? 2 * NDS : 0;
     constexpr int NPV = DO_PV ? 4 * NDB : 0;
     constexpr int N = NS + NPV;
@@ -176,7 +224,7 @@ struct Wave {
       const int i = idx(j);
       if (is_s(j)) {
         const int ds = i >> 1, kb = i & 1;
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j], qf[ds], s[kb], 0, 0, 0);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j], qf.v[ds], s[kb], 0, 0, 0);
       } else {
         const int kbc = i / NDB, db = i % NDB;
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j], pf[kbc >> 1][kbc & 1], o[db], 0, 0, 0);
@@ -184,6 +232,56 @@ struct Wave {
       if (j + LA < N) load(j + LA);
       __builtin_amdgcn_sched_barrier(0);
     }
+  }
+
+  // fp8 MFMA phase: S^T = K Q^T with v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3 operands,
+  // unit block scales; 2 * D / 64 steps of 64 d, each reading 32 bytes of K per lane,
+  // twice the work of a bf16 step), and the bf16 O^T += V^T P^T steps as above. One
+  // S step precedes every R = NPV / NS PV steps. Operand reads go in 16-byte units,
+  // kLookahead units ahead, pinned by a scheduling fence after every step.
+  template <int KS, int VS, bool DO_S, bool DO_PV>
+  __device__ __forceinline__ void mfma_phase_fp8(const char* smem) {
+    using L = Lds<D, QK8>;
+    using Pl = Fp8Plan<DO_S ? 2 * NDS : 0, DO_PV ? 4 * NDB : 0>;
+    const char* kb_ = smem + k_rd + KS * L::KTILE;
+    const char* vb_ = smem + v_rd + VS * L::VTILE;
+    i32x8 sf[Pl::NS > 0 ? Pl::NS : 1];
+    bf16x8 vf[Pl::NPV > 0 ? Pl::NPV : 1];
+    auto load_unit = [&](auto U) {
+      constexpr int u = decltype(U)::value;
+      if constexpr (u < Pl::NU) {
+        constexpr int j = Pl::unit_step(u);
+        constexpr int i = Pl::idx(j);
+        if constexpr (Pl::is_s(j)) {
+          constexpr int h = u - Pl::ustart(j), ds = i >> 1, kb = i & 1;
+          const u32x4 x = *reinterpret_cast<const u32x4*>(kb_ + kb * 32 * L::KP + ds * 64 + 16 * h);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sf[i][4 * h + e] = (int)x[e];
+        } else {
+          constexpr int kbc = i / NDB, db = i % NDB;
+          vf[i] = *reinterpret_cast<const bf16x8*>(vb_ + db * 32 * L::VP + 32 * kbc);
+        }
+      }
+    };
+    if (DO_S) {
+      s[0] = f32x16{};
+      s[1] = f32x16{};
+    }
+    static_for<0, Pl::LA>(load_unit);
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, Pl::N>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      constexpr int i = Pl::idx(j);
+      if constexpr (Pl::is_s(j)) {
+        constexpr int ds = i >> 1, kb = i & 1;
+        s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(sf[i], qf.v[ds], s[kb], 0, 0, 0, 127, 0, 127);
+      } else {
+        constexpr int kbc = i / NDB, db = i % NDB;
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf[kbc >> 1][kbc & 1], o[db], 0, 0, 0);
+      }
+      static_for<Pl::ustart(j) + Pl::LA, Pl::ustart(j + 1) + Pl::LA>(load_unit);
+      __builtin_amdgcn_sched_barrier(0);
+    });
   }
 
   // Softmax phase of tile t: online softmax of S_t (exp2 domain, lazy rescale) -> P_t.
@@ -255,18 +353,19 @@ struct Wave {
 // Group 0 (waves 0-3) owns V: a unit is 4 keys x 8 d, transposed in registers and
 // written as 8-byte key groups of 8 V^T rows; the 16 lanes of a write pass cover
 // the 16 key groups of one row.
-template <int D>
+template <int D, bool QK8>
 struct Stager {
-  static constexpr int KCH = D / 8;                 // 16-byte chunks per K row
+  static constexpr int KCH = QK8 ? D / 16 : D / 8;  // 16-byte chunks per K row
+  static constexpr int VCH = D / 8;                 // 16-byte chunks per V row
   static constexpr int GT = kThreads / 2;           // threads per group
   static constexpr int KLOADS = kBK * KCH / GT;     // K chunks per thread
   static constexpr int KROWS = GT / KCH;            // K rows per load round
-  static constexpr int VUNITS = (kBK / 4) * KCH;    // V units per tile
+  static constexpr int VUNITS = (kBK / 4) * VCH;    // V units per tile
   static constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw 32-bit buffer, no swizzle
   u32x4 r[4];
-  const __bf16* src;     // K or V rows of this (b, h) starting at the partition
-  int64_t row_stride;    // elements
-  int stride_bytes;
+  const char* src;       // K or V rows of this (b, h) starting at the partition
+  int stride_bytes;      // between rows
+  int row_bytes;         // D elements
   int n;                 // keys in the partition
   int voff[4];           // byte offsets of this thread's loads within a tile
   int w_off;             // LDS write base of this thread
@@ -277,8 +376,8 @@ struct Stager {
   // branch or a clamp per lane. A tile past the end gets an empty range.
   __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(int tile) const {
     const int rows = n - tile * kBK;
-    const int bytes = rows > 0 ? (min(rows, kBK) - 1) * stride_bytes + D * 2 : 0;
-    const uint64_t base = reinterpret_cast<uint64_t>(src + (int64_t)(rows > 0 ? tile * kBK : 0) * row_stride);
+    const int bytes = rows > 0 ? (min(rows, kBK) - 1) * stride_bytes + row_bytes : 0;
+    const uint64_t base = reinterpret_cast<uint64_t>(src + (int64_t)(rows > 0 ? tile * kBK : 0) * stride_bytes);
     // all of it is wave-uniform; readfirstlane keeps the descriptor in SGPRs
     const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base);
     const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32));
@@ -292,7 +391,7 @@ struct Stager {
   }
   template <int SLOT>
   __device__ __forceinline__ void store_k(char* smem) {
-    using L = Lds<D>;
+    using L = Lds<D, QK8>;
 #pragma unroll
     for (int j = 0; j < KLOADS; ++j)
       *reinterpret_cast<u32x4*>(smem + w_off + SLOT * L::KTILE + j * KROWS * L::KP) = r[j];
@@ -305,7 +404,7 @@ struct Stager {
   }
   template <int SLOT>
   __device__ __forceinline__ void store_v(char* smem) {
-    using L = Lds<D>;
+    using L = Lds<D, QK8>;
     if (!on) return;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -328,12 +427,12 @@ struct Stager {
 // stages K (tile t+2 during Y_t), group 0 stages V (tile t during Y_t); two LDS
 // slots per operand suffice for this offset: a slot is rewritten only after both
 // groups' last read of its previous tile.
-template <int D, bool OUT_BF16>
+template <int D, bool OUT_BF16, bool QK8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_kernel(const AttnArgs a) {
-  using L = Lds<D>;
-  using W = Wave<D>;
-  using St = Stager<D>;
+  using L = Lds<D, QK8>;
+  using W = Wave<D, QK8>;
+  using St = Stager<D, QK8>;
   static_assert(kQB == 1 && St::KLOADS >= 1 && St::KLOADS <= 4 && St::VUNITS <= St::GT, "tile shape");
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
 
@@ -370,12 +469,27 @@ void attn_bf16_kernel(const AttnArgs a) {
   }
 
   W w;
-  const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + b * a.q_sb + hh * a.q_sh;
   const int qrow = q0 + wave * kRowsPerWave + l32;
+  if constexpr (QK8) {
+    const unsigned char* qp = reinterpret_cast<const unsigned char*>(a.q) + b * a.q_sb + hh * a.q_sh +
+                              (int64_t)min(qrow, a.Sq - 1) * a.q_ss + 32 * half;
 #pragma unroll
-  for (int ds = 0; ds < W::NDS; ++ds) {
-    const u32x4 x = *reinterpret_cast<const u32x4*>(qp + (int64_t)min(qrow, a.Sq - 1) * a.q_ss + ds * 16 + 8 * half);
-    w.qf[ds] = __builtin_bit_cast(bf16x8, qrow < a.Sq ? x : u32x4{0u, 0u, 0u, 0u});
+    for (int ds = 0; ds < W::NDS; ++ds) {
+      const u32x4 x0 = *reinterpret_cast<const u32x4*>(qp + 64 * ds);
+      const u32x4 x1 = *reinterpret_cast<const u32x4*>(qp + 64 * ds + 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        w.qf.v[ds][e] = qrow < a.Sq ? (int)x0[e] : 0;
+        w.qf.v[ds][4 + e] = qrow < a.Sq ? (int)x1[e] : 0;
+      }
+    }
+  } else {
+    const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + b * a.q_sb + hh * a.q_sh;
+#pragma unroll
+    for (int ds = 0; ds < W::NDS; ++ds) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(qp + (int64_t)min(qrow, a.Sq - 1) * a.q_ss + ds * 16 + 8 * half);
+      w.qf.v[ds] = __builtin_bit_cast(bf16x8, qrow < a.Sq ? x : u32x4{0u, 0u, 0u, 0u});
+    }
   }
 #pragma unroll
   for (int db = 0; db < W::NDB; ++db) w.o[db] = f32x16{};
@@ -385,25 +499,29 @@ void attn_bf16_kernel(const AttnArgs a) {
     for (int c = 0; c < 2; ++c) w.pf[kb][c] = bf16x8{};
   w.m = -INFINITY;
   w.l = 0.f;
-  w.k_rd = l32 * L::KP + 16 * half;
+  w.k_rd = l32 * L::KP + (QK8 ? 32 : 16) * half;
   w.v_rd = L::V0 + l32 * L::VP + 16 * half;
-  const float c2 = a.scale_log2;
+  // fp8 scores are in units of the two dequantisation factors of this (b, h)
+  const float c2 = QK8 ? a.scale_log2 * a.q_scale[bh] * a.k_scale[bh] : a.scale_log2;
   const int T = (n + kBK - 1) / kBK;
 
   St st;
   st.n = n;
-  st.row_stride = a.k_ss;
-  st.stride_bytes = (int)(a.k_ss * 2);
-  const int64_t kv_off = b * a.k_sb + hh * a.k_sh + (int64_t)ks * a.k_ss;
+  const int64_t kv_off = b * a.k_sb + hh * a.k_sh + (int64_t)ks * a.k_ss;   // elements
   if (grp == 1) {
-    st.src = reinterpret_cast<const __bf16*>(a.k) + kv_off;
+    constexpr int ek = QK8 ? 1 : 2;   // bytes per K element
+    st.stride_bytes = (int)(a.k_ss * ek);
+    st.row_bytes = D * ek;
+    st.src = reinterpret_cast<const char*>(a.k) + kv_off * ek;
     const int row = gtid / St::KCH, ch = gtid % St::KCH;
 #pragma unroll
     for (int j = 0; j < 4; ++j) st.voff[j] = (row + j * St::KROWS) * st.stride_bytes + ch * 16;
     st.w_off = row * L::KP + ch * 16;
     st.on = true;
   } else {
-    st.src = reinterpret_cast<const __bf16*>(a.v) + kv_off;
+    st.stride_bytes = (int)(a.k_ss * 2);
+    st.row_bytes = D * 2;
+    st.src = reinterpret_cast<const char*>(a.v) + kv_off * 2;
     const int va = gtid & 15, vc = gtid >> 4;   // 4-key group, 8-wide d chunk
 #pragma unroll
     for (int j = 0; j < 4; ++j) st.voff[j] = (4 * va + j) * st.stride_bytes + vc * 16;
@@ -610,12 +728,22 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream) {
   if (total <= 0) return hipSuccess;
   if (total > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)total), block(kThreads);
-  if (a.D == 128) {
-    if (a.out_bf16) hipLaunchKernelGGL((attn_bf16_kernel<128, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<128, false>), grid, block, 0, stream, a);
+  if (a.qk_fp8) {
+    if (a.D == 128) {
+      if (a.out_bf16) hipLaunchKernelGGL((attn_bf16_kernel<128, true, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((attn_bf16_kernel<128, false, true>), grid, block, 0, stream, a);
+    } else if (a.D == 64) {
+      if (a.out_bf16) hipLaunchKernelGGL((attn_bf16_kernel<64, true, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((attn_bf16_kernel<64, false, true>), grid, block, 0, stream, a);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else if (a.D == 128) {
+    if (a.out_bf16) hipLaunchKernelGGL((attn_bf16_kernel<128, true, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_bf16_kernel<128, false, false>), grid, block, 0, stream, a);
   } else if (a.D == 64) {
-    if (a.out_bf16) hipLaunchKernelGGL((attn_bf16_kernel<64, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<64, false>), grid, block, 0, stream, a);
+    if (a.out_bf16) hipLaunchKernelGGL((attn_bf16_kernel<64, true, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_bf16_kernel<64, false, false>), grid, block, 0, stream, a);
   } else {
     return hipErrorInvalidValue;
   }

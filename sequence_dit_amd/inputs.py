@@ -53,6 +53,10 @@ class Workload:
     q1: Optional[torch.Tensor] = None
     k1: Optional[torch.Tensor] = None
     v1: Optional[torch.Tensor] = None
+    q8: Optional[torch.Tensor] = None        # fp8 E4M3 codes of q (fp8-input workloads)
+    k8: Optional[torch.Tensor] = None
+    q_scale: Optional[torch.Tensor] = None   # float32 [B, H]: a code stands for code * scale
+    k_scale: Optional[torch.Tensor] = None
     near: List[int] = field(default_factory=list)
     merge_order: List[int] = field(default_factory=list)
 
@@ -231,6 +235,35 @@ def small_case(seed: int, B: int, H: int, Sq: int, Skv: int, D: int, ranges: Seq
     return Workload(f"small case seed {seed}", B, H, Sq, Skv, D, dtype,
                     to_dtype(q, dtype), to_dtype(k, dtype), to_dtype(v, dtype),
                     list(ranges), 0, D ** -0.5)
+
+
+FP8_MAX = 448.0   # largest finite E4M3 ("e4m3fn") magnitude
+
+
+def quantize_fp8(x: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per-(b, h) fp8 E4M3 codes of x [B, H, S, D] and float32 factors [B, H].
+
+    factor = amax / 448 over the (b, h) slice (1 for an all-zero slice); codes are
+    torch's float8_e4m3fn cast (round to nearest even) of x / factor, whose
+    magnitude is at most 448 up to one fp32 rounding, so no code overflows. A code
+    stands for its value times the factor of its (b, h).
+    """
+    xf = x.float()
+    amax = xf.abs().amax(dim=(2, 3))
+    factor = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax)).contiguous()
+    codes = (xf / factor[:, :, None, None]).to(torch.float8_e4m3fn)
+    return codes, factor
+
+
+def small_case_fp8(seed: int, B: int, H: int, Sq: int, Skv: int, D: int, ranges: Sequence[Range],
+                   std: float = 1.0) -> Workload:
+    """small_case with fp8 queries and keys: w.q8, w.k8 (float8_e4m3fn codes) and
+    w.q_scale, w.k_scale (float32 [B, H]) are attached; v stays bf16."""
+    w = small_case(seed, B, H, Sq, Skv, D, ranges, torch.bfloat16, std)
+    w.q8, w.q_scale = quantize_fp8(w.q)
+    w.k8, w.k_scale = quantize_fp8(w.k)
+    w.name = f"fp8 {w.name}"
+    return w
 
 
 WORKLOADS = {1: tiny_fp32, 2: image_dit, 3: video_dit, 4: long_video, 5: selective_reuse}

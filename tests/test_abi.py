@@ -317,3 +317,38 @@ def test_compose_groups_rejects(kw, status, text):
 
 def test_compose_groups_zero_rows_ok_without_gpu():
     assert compose_call(rows=0)[0] == N.AS_OK
+
+
+def attn_fp8(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, qsc=FAKE, ksc=FAKE, B=1, H=2, Sq=16, Skv=64, D=128,
+                qs=(4096, 2048, 128), kvs=(16384, 8192, 128), ranges=[(0, 32), (32, 64)],
+                scale=0.088, state=N.AS_F32, out=FAKE, lse=FAKE)
+    args.update(kw)
+    flat = [x for r in args["ranges"] for x in r]
+    rng = (ctypes.c_int32 * max(1, len(flat)))(*flat)
+    st = N.lib().as_partition_attn_fp8(args["q"], args["k"], args["v"], args["qsc"], args["ksc"], args["B"],
+                                       args["H"], args["Sq"], args["Skv"], args["D"], N._i64(args["qs"]),
+                                       N._i64(args["kvs"]), rng, len(args["ranges"]), args["scale"],
+                                       args["state"], args["out"], args["lse"], None)
+    return st, N.lib().as_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(qsc=0), N.AS_ERR_INVALID_ARG, "q_scale and k_scale"),
+    (dict(ksc=0), N.AS_ERR_INVALID_ARG, "q_scale and k_scale"),
+    (dict(ksc=FAKE + 2), N.AS_ERR_INVALID_ARG, "4-byte aligned"),
+    (dict(D=96, qs=(3072, 1536, 96), kvs=(12288, 6144, 96)), N.AS_ERR_UNSUPPORTED, "fp8"),
+    (dict(qs=(4096, 2048, 136)), N.AS_ERR_INVALID_ARG, "multiples of 16"),
+    (dict(kvs=(16384, 8192, 136)), N.AS_ERR_INVALID_ARG, "multiples of 16"),
+    (dict(state=7), N.AS_ERR_INVALID_ARG, "state_dtype"),
+    (dict(q=FAKE + 8), N.AS_ERR_INVALID_ARG, "aligned"),
+    (dict(ranges=[(0, 65)]), N.AS_ERR_INVALID_ARG, "kv_ranges[0]"),
+])
+def test_partition_attn_fp8_rejects(kw, status, text):
+    st, msg = attn_fp8(**kw)
+    assert st == status, msg
+    assert text in msg
+
+
+def test_partition_attn_fp8_empty_problem_is_ok_without_gpu():
+    assert attn_fp8(Sq=0, q=0, out=0, lse=0, qsc=0, ksc=0)[0] == N.AS_OK

@@ -106,6 +106,73 @@ def test_bf16_large_logits_stay_finite():
     check_states(out, lse, o_ref, l_ref, BF16_OUT, 1e-3 * 100, "bf16 x100 logits")
 
 
+def fp8_reference(w, q8, k8, q_scale, k_scale, ranges, scale):
+    """Oracle states on the values the fp8 codes stand for (decoded by the oracle)."""
+    qd = oracle.fp8.dequantize(q8.cpu().view(torch.uint8).numpy(), q_scale.cpu().numpy())
+    kd = oracle.fp8.dequantize(k8.cpu().view(torch.uint8).numpy(), k_scale.cpu().numpy())
+    return oracle.partition_states(qd, kd, w.v if w is not None else None, ranges, scale)
+
+
+@pytest.mark.parametrize("state", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("D", [128, 64])
+def test_fp8_small_ragged(D, state):
+    """fp8 E4M3 q/k with per-(b, h) factors, bf16 v: ragged, single-key, empty, overlapping and full ranges."""
+    w = inputs.small_case_fp8(50 + D, 2, 3, 300, 1000, D, RAGGED)
+    note(f"fp8 small ragged D={D} state={state} B=2 H=3 Sq=300 Skv=1000 P={len(RAGGED)}")
+    out, lse = N.partition_attn_fp8(to_dev(w.q8), to_dev(w.k8), to_dev(w.v), to_dev(w.q_scale),
+                                    to_dev(w.k_scale), w.ranges, w.scale, state_dtype=state)
+    torch.cuda.synchronize()
+    o_ref, l_ref = fp8_reference(w, w.q8, w.k8, w.q_scale, w.k_scale, w.ranges, w.scale)
+    check_states(out.float(), lse, o_ref, l_ref, BF16_OUT, BF16_LSE, f"fp8 D={D} {state}")
+
+
+def test_fp8_path_equals_bf16_path_on_the_same_values():
+    """Codes of moderate size with factors 1 are exact in bf16, so both paths score the same Q and K.
+    The fp8 MFMA sums 64 products per instruction and rounds differently from four bf16 MFMAs (LSE
+    differences up to ~2e-4 were seen on LSE values of 8-16), and P's bf16 rounding can flip with it;
+    both stay inside the oracle tolerances. A K/Q byte-order slip in the fp8 operands would give O(1)
+    differences."""
+    w = inputs.small_case(77, 1, 2, 257, 700, 128, [(0, 700), (3, 300), (650, 700)])
+    q8 = (2 * w.q.float()).to(torch.float8_e4m3fn)
+    k8 = (2 * w.k.float()).to(torch.float8_e4m3fn)
+    ones = torch.ones(1, 2, device=DEV)
+    note("fp8 path vs bf16 path on identical values")
+    o8, l8 = N.partition_attn_fp8(to_dev(q8), to_dev(k8), to_dev(w.v), ones, ones, w.ranges, w.scale)
+    o16, l16 = N.partition_attn(to_dev(q8.to(torch.bfloat16)), to_dev(k8.to(torch.bfloat16)), to_dev(w.v),
+                                w.ranges, w.scale)
+    torch.cuda.synchronize()
+    assert (l8 - l16).abs().max().item() <= BF16_LSE
+    assert (o8 - o16).abs().max().item() <= 1e-2
+
+
+def test_fp8_strided_inputs_and_guarded_outputs():
+    """fp8 views with padded rows and an extra head; outputs followed by canaries."""
+    D, B, H, Sq, Skv = 128, 1, 2, 130, 333
+    w = inputs.small_case_fp8(22, B, H, Sq, Skv, D, [(0, 333), (5, 70), (300, 333)])
+    qbig = torch.zeros(B, H, Sq + 16, D + 16, dtype=torch.uint8)
+    qbig[:, :, 8:8 + Sq, :D] = w.q8.view(torch.uint8)
+    kbig = torch.zeros(B, H + 1, Skv, D + 16, dtype=torch.uint8)
+    vbig = torch.zeros(B, H + 1, Skv, D + 16, dtype=torch.bfloat16)
+    kbig[:, 1:, :, :D] = w.k8.view(torch.uint8)
+    vbig[:, 1:, :, :D] = w.v
+    fp8 = torch.float8_e4m3fn
+    qd = to_dev(qbig).view(fp8)[:, :, 8:8 + Sq, :D]
+    kd = to_dev(kbig).view(fp8)[:, 1:, :, :D]
+    vd = to_dev(vbig)[:, 1:, :, :D]
+    P = len(w.ranges)
+    n_out, n_lse = P * B * H * Sq * D, P * B * H * Sq
+    guard = 4096
+    obuf = torch.full((n_out + guard,), 12345.0, device=DEV)
+    lbuf = torch.full((n_lse + guard,), 12345.0, device=DEV)
+    note("fp8 strided views + guarded outputs")
+    out, lse = N.partition_attn_fp8(qd, kd, vd, to_dev(w.q_scale), to_dev(w.k_scale), w.ranges, w.scale,
+                                    out=obuf[:n_out].view(P, B, H, Sq, D), lse=lbuf[:n_lse].view(P, B, H, Sq))
+    torch.cuda.synchronize()
+    assert torch.all(obuf[n_out:] == 12345.0) and torch.all(lbuf[n_lse:] == 12345.0), "write past the end"
+    o_ref, l_ref = fp8_reference(w, w.q8, w.k8, w.q_scale, w.k_scale, w.ranges, w.scale)
+    check_states(out, lse, o_ref, l_ref, BF16_OUT, BF16_LSE, "fp8 strided")
+
+
 def test_f32_tiny_workload_shuffled_merge_equals_full_attention():
     """The tiny fp32 workload: states, then a merge in shuffled order, equal full attention within 1e-5."""
     w = inputs.tiny_fp32()
@@ -427,6 +494,29 @@ def test_full_size_image_and_video(cfg):
                  f"config {cfg} merged")
 
 
+def fp8_full_size_check(w, q8, k8, qs, ks, heads, rs, what):
+    """fp8 states of a full-size workload against the oracle on sampled rows of the decoded inputs."""
+    out, lse = N.partition_attn_fp8(q8, k8, w.v_dev, qs, ks, w.ranges, w.scale)
+    torch.cuda.synchronize()
+    qsel = q8[:, heads][:, :, rs].cpu()
+    ksel = k8[:, heads].cpu()
+    qd = oracle.fp8.dequantize(qsel.view(torch.uint8).numpy(), qs[:, heads].cpu().numpy())
+    kd = oracle.fp8.dequantize(ksel.view(torch.uint8).numpy(), ks[:, heads].cpu().numpy())
+    o_ref, l_ref = oracle.partition_states(qd, kd, w.v[:, heads], w.ranges, w.scale)
+    check_states(out[:, :, heads][:, :, :, rs], lse[:, :, heads][:, :, :, rs], o_ref, l_ref, BF16_OUT, BF16_LSE,
+                 what)
+
+
+def test_full_size_video_fp8():
+    """Video DiT shape (D = 64, masked tiles) with fp8 q/k at full size, sampled rows."""
+    w = inputs.make(3)
+    note(f"full size fp8 workload: {w.name}")
+    q8, qs = inputs.quantize_fp8(to_dev(w.q))
+    k8, ks = inputs.quantize_fp8(to_dev(w.k))
+    w.v_dev = to_dev(w.v)
+    fp8_full_size_check(w, q8, k8, qs, ks, [0, w.H // 2, w.H - 1], sample_rows(w.Sq, seed=13), "video fp8")
+
+
 @pytest.fixture(scope="module")
 def reuse_workload():
     return inputs.selective_reuse()
@@ -497,3 +587,14 @@ def test_full_size_long_video_and_selective_reuse(reuse_workload):
     note(f"planner: local drift {runner.local_drift.item():.4g}, alpha near/far "
          f"{alpha[w.near].mean():.3f}/{np.delete(alpha, w.near).mean():.3f}, "
          f"group errors {np.array2string(gpu_ase, precision=2)}, compute {plan['compute'].cpu().numpy().tolist()}")
+
+
+def test_full_size_long_video_fp8(reuse_workload):
+    """Long-video anchor shape (32 partitions of 3840, D = 128) with fp8 q/k, as bench.py times it."""
+    w = reuse_workload
+    note(f"full size fp8 workload: {w.name}")
+    q8, qs = inputs.quantize_fp8(to_dev(w.q))
+    k8, ks = inputs.quantize_fp8(to_dev(w.k))
+    w.v_dev = to_dev(w.v)
+    fp8_full_size_check(w, q8, k8, qs, ks, [0, 11, 23], sample_rows(w.Sq, n=16, seed=6), "long video fp8")
+    del w.v_dev
