@@ -27,6 +27,9 @@ sys.path.insert(0, ROOT)
 METRIC = "partition-attn TFLOP/s (% bf16 MFMA peak) + as_merge GB/s (% HBM peak), 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+# S = K Q^T (half the FLOPs) at the fp8 peak, PV (the other half) at the bf16 peak
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_MIXED_TFLOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "partition_attn_traffic.txt")
 ATTN_SOURCE = os.path.join(ROOT, "sequence_dit_amd", "csrc", "partition_attn.hip")
 
@@ -302,6 +305,40 @@ def main():
         kernels["state_bytes_per_row"] = {"fp32": 4 * w.D + 4, "bf16": 2 * w.D + 4,
                                           "kv_bytes_per_key_bf16": 4 * w.D}
         del st16, c16, g16
+
+        # fp8 E4M3 queries and keys (per-(b, h) factors; the quantisation is the caller's input
+        # preparation and is not timed): the anchor over all partitions and the fresh partitions
+        # of the next step, against the peak of their mix (S on the fp8 MFMA, PV on the bf16 MFMA)
+        q8, qs8 = inputs.quantize_fp8(q)
+        k8, ks8 = inputs.quantize_fp8(k)
+        q18, qs18 = inputs.quantize_fp8(q1)
+        k18, ks18 = inputs.quantize_fp8(k1)
+        near_ranges = [w.ranges[i] for i in near]
+        f_out = torch.empty((len(near),) + tuple(runner.state_out.shape[1:]), dtype=torch.float32, device=dev)
+        f_lse = torch.empty((len(near),) + tuple(runner.state_lse.shape[1:]), dtype=torch.float32, device=dev)
+
+        def fp8_calls():
+            runner._timed("attn_anchor_fp8", N.partition_attn_fp8, q8, k8, v, qs8, ks8, w.ranges, w.scale,
+                          out=runner.state_out, lse=runner.state_lse)
+            runner._timed("attn_fresh_fp8", N.partition_attn_fp8, q18, k18, v1, qs18, ks18, near_ranges, w.scale,
+                          out=f_out, lse=f_lse)
+
+        runner.timer = None
+        fp8_calls()
+        torch.cuda.synchronize()
+        runner.timer = []
+        for _ in range(max(1, args.steps // 2)):
+            fp8_calls()
+        torch.cuda.synchronize()
+        ftimes = {}
+        for name, s, e in runner.timer:
+            ftimes.setdefault(name, []).append(s.elapsed_time(e))
+        for name, base in (("attn_anchor_fp8", "attn_anchor"), ("attn_fresh_fp8", "attn_fresh")):
+            ms = sum(ftimes[name]) / len(ftimes[name])
+            tf = attn_flops[base] / ms / 1e9
+            kernels[name] = {"ms": round(ms, 4), "TFLOP/s": round(tf, 1), "frac_mixed_peak": round(tf / PEAK_MIXED_TFLOPS, 4),
+                             "speedup_vs_bf16": round(kernels[base]["ms"] / ms, 3)}
+        del q8, k8, q18, k18, f_out, f_lse
 
     traffic = measured_traffic()
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
