@@ -393,6 +393,22 @@ NORM_RTOL = 1e-6   # fp64 sums rounded once to fp32 (unit roundoff 2^-24)
 PLAN_RTOL = 1e-5   # fp32 arithmetic on a few terms per output
 
 
+def test_contribution_large_lse_values():
+    """LSE values near 1000 (scores of a x100 logit scale): the weights are softmaxes of LSE
+    differences and must keep fp32 accuracy; forming L* = M + ln S first would round it to
+    the ulp of M (6e-5 at 1000)."""
+    g = np.random.default_rng(41)
+    P, rows = 32, 1000
+    lse = (1000.0 + 3.0 * g.standard_normal((P, rows))).astype(np.float32)
+    lse[3, :50] = -np.inf
+    note("contribution with LSE ~ 1000")
+    w, sc = N.partition_contribution(torch.from_numpy(lse).to(DEV), 250)
+    torch.cuda.synchronize()
+    w_ref, s_ref = oracle.contribution(lse, 250)
+    assert np.abs(w.cpu().double().numpy() - w_ref).max() <= F32_TOL
+    assert np.abs(sc.cpu().double().numpy() - s_ref).max() <= F32_TOL
+
+
 @pytest.mark.parametrize("diff", [False, True])
 @pytest.mark.parametrize("P,n", [(1, 4), (3, 4100), (5, 0), (32, 300 * 128), (256, 64), (2, 3 * 262144 + 20),
                                  (1, 24 * 3840 * 128)])
