@@ -21,12 +21,20 @@
 //     loads of a tile are issued one tile ahead of its LDS store.
 //   * The 8 waves form two groups that alternate an MFMA phase with a softmax phase,
 //     one phase apart, so that on every SIMD one wave's softmax runs beside the
-//     other's MFMAs (a wave does not overlap its own VALU work with its MFMAs).
+//     other's MFMAs; each wave's code stays a plain sequence of phases.
 //   * Online softmax in the exp2 domain with a lazy rescale: the running max is
 //     only moved (and O, l rescaled) when a new score exceeds it by more than
 //     2^64, which is exact because the same max is used for O and l.
 //   * Workgroups sharing a (batch, head, partition) are mapped to the same XCD so
 //     that its L2 serves their common K/V tiles.
+//
+// fp8 queries and keys (template flag QK8): Q and K are FP8 E4M3 codes and
+// S^T = K Q^T runs on v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales), 2 D/64
+// steps per tile of 32 bytes of K per lane; K rows in LDS are D + 16 bytes. The
+// per-(batch, head) dequantisation factors fold into the softmax scale. Softmax,
+// P, V and PV are the bf16 path's.
+//   DiTango review page, reference list: SageAttention (8-bit attention for
+//   inference); FastUSP page, prior work: the FP8 formats paper (E4M3).
 #include <hip/hip_runtime.h>
 #include <math.h>
 
