@@ -119,6 +119,47 @@ def cpu_baseline(w, target_s, reuse):
 # GPU bench
 # --------------------------------------------------------------------------- #
 
+def shape_sweep(N, inputs, torch, dev, reps=10):
+    """a1 alone on the image DiT and video DiT workloads, warm (back-to-back launches, inputs
+    and states in the 256 MB MALL where they fit) and cold (a 512 MB scratch write between
+    launches, outside the events). Median launch time; the fraction is max(t_MFMA, t_HBM) / t
+    with the algorithmic FLOP and bytes of the launch."""
+    res = {}
+    scratch = torch.empty(512 << 18, dtype=torch.float32, device=dev)
+    for cfg, name in ((2, "image"), (3, "video")):
+        w = inputs.make(cfg)
+        q, k, v = w.q.to(dev), w.k.to(dev), w.v.to(dev)
+        out = torch.empty((w.P, w.B, w.H, w.Sq, w.D), dtype=torch.float32, device=dev)
+        lse = torch.empty((w.P, w.B, w.H, w.Sq), dtype=torch.float32, device=dev)
+        keys = sum(e - s for s, e in w.ranges)
+        flops = 4 * w.B * w.H * w.Sq * keys * w.D
+        nbytes = 2 * w.B * w.H * (w.Sq * w.D + 2 * keys * w.D) + w.P * w.B * w.H * w.Sq * (4 * w.D + 4)
+        t_floor = max(flops / (PEAK_BF16_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBPS * 1e9)) * 1e3
+        for mode in ("warm", "cold"):
+            for _ in range(3):
+                N.partition_attn(q, k, v, w.ranges, w.scale, out=out, lse=lse)
+            # no host synchronisation inside the loop: an idle GPU between launches would
+            # start the next one at a lower clock
+            ev = []
+            for _ in range(reps):
+                if mode == "cold":
+                    scratch.fill_(1.0)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                N.partition_attn(q, k, v, w.ranges, w.scale, out=out, lse=lse)
+                b.record()
+                ev.append((a, b))
+            torch.cuda.synchronize()
+            ms = sorted(a.elapsed_time(b) for a, b in ev)
+            t = ms[len(ms) // 2]
+            res[f"attn_{name}_{mode}"] = {"ms": round(t, 4), "TFLOP/s": round(flops / t / 1e9, 1),
+                                          "frac_mfma": round(flops / t / 1e9 / PEAK_BF16_TFLOPS, 4),
+                                          "frac_roofline": round(t_floor / t, 4)}
+        del q, k, v, out, lse
+    del scratch
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -345,6 +386,10 @@ def main():
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "algorithmic_flops_per_launch": attn_total_flops / attn_launches,
                 "avg_launch_ms": round(attn_ms / attn_launches, 4)}
+
+    if reuse:
+        log("image and video DiT shapes, warm and cold")
+        kernels.update(shape_sweep(N, inputs, torch, dev))
 
     cpu = None
     if not args.no_cpu_baseline:
