@@ -5,7 +5,8 @@
 //   partition is its partial attention output with the log-sum-exp of its scores.
 //
 // bf16 kernel design (one workgroup = 8 waves = 256 query rows x one (batch, head)
-// x one partition; one wave = 32 query rows; two waves per SIMD):
+// x one partition; one wave = 32 query rows; two waves per SIMD; key tiles of 64
+// keys at D = 128 and 128 at D = 64):
 //   * The scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16
 //     (M = 32 keys, N = 32 queries, K = 16 of D). In that accumulator layout a lane
 //     holds 16 keys of ONE query row, so the row max needs one cross-half swap
@@ -15,7 +16,7 @@
 //     P never leaves registers.
 //   * Q stays in registers for the whole partition. K tiles are staged in LDS as
 //     [key][d] rows padded to 2D + 16 bytes; V tiles are transposed in registers on
-//     their way into LDS ([d][key] rows of 64 keys padded to 144 bytes, 4-key groups
+//     their way into LDS ([d][key] rows of a tile's keys padded by 16 bytes, 4-key groups
 //     placed so that one 16-byte read per lane is the V^T operand). The padding makes
 //     the 16-byte operand reads conflict-free. Two slots per operand: the global
 //     loads of a tile are issued one tile ahead of its LDS store.
@@ -74,7 +75,15 @@ constexpr int kWaves = 8;
 constexpr int kQB = 1;                       // 32-row query blocks per wave
 constexpr int kRowsPerWave = 32 * kQB;       // 32
 constexpr int kBQ = kWaves * kRowsPerWave;   // 256 query rows per workgroup
-constexpr int kBK = 64;                      // keys per tile
+// Keys per tile: 64 at D = 128. At D = 64 a tile's MFMA work halves while its
+// softmax work does not, so the softmax phase is the longer one and every phase
+// pays its start, drain and barrier for half the work; a 128-key tile (the
+// registers allow twice the S and P of a 64-key one there) halves those costs.
+template <int D>
+struct Tile {
+  static constexpr int KB = D == 64 ? 128 : 64;   // keys per tile
+  static constexpr int NKB = KB / 32;             // 32-key MFMA blocks per tile
+};
 constexpr int kThreads = kWaves * 64;
 constexpr float kRescaleThreshold = 64.0f;   // log2 units: probabilities stay <= 2^64
 
@@ -153,14 +162,14 @@ struct Fp8Plan {
 template <int D, bool QK8>
 struct Lds {
   static constexpr int KP = D * (QK8 ? 1 : 2) + 16;   // K row pitch (fp8 or bf16 keys)
-  static constexpr int KTILE = kBK * KP;
-  static constexpr int VP = kBK * 2 + 16;      // V^T row pitch
+  static constexpr int KTILE = Tile<D>::KB * KP;
+  static constexpr int VP = Tile<D>::KB * 2 + 16;   // V^T row pitch
   static constexpr int VTILE = D * VP;
   static constexpr int V0 = 2 * KTILE;         // two K slots, then two V slots
   static constexpr int BYTES = 2 * KTILE + 2 * VTILE;
 };
 
-// Position (bytes) of 4-key group g (keys 4g..4g+3 of a 64-key tile) in a V^T row.
+// Position (bytes) of 4-key group g (keys 4g..4g+3 of a tile) in a V^T row.
 // The MFMA operand of lane half h for (key block kb, step c) is the key groups
 // 8kb+4c+h and 8kb+4c+h+2, stored side by side as 16-byte chunk 4kb+2c+h.
 __device__ __forceinline__ constexpr int vt_group_pos(int g) {
@@ -178,9 +187,10 @@ template <int D, bool QK8>
 struct Wave {
   static constexpr int NDS = QK8 ? D / 64 : D / 16;   // MFMA k-steps of S^T = K Q^T
   static constexpr int NDB = D / 32;                  // 32-wide d blocks of O^T
+  static constexpr int KB = Tile<D>::KB, NKB = Tile<D>::NKB;
   QFrag<D, QK8> qf;      // Q, for the whole partition
-  f32x16 s[2];           // S^T of the current tile: [kb], reg r <-> key 32kb + 8(r/4) + 4half + r%4
-  bf16x8 pf[2][2];       // P of the previous tile, B operand of O^T: [kb][c]
+  f32x16 s[NKB];         // S^T of the current tile: [kb], reg r <-> key 32kb + 8(r/4) + 4half + r%4
+  bf16x8 pf[NKB][2];     // P of the previous tile, B operand of O^T: [kb][c]
   f32x16 o[NDB];         // O^T: [db], reg r <-> d = 32db + 8(r/4) + 4half + r%4
   float m, l;            // running max (log2 domain, scaled) and row sum
   int k_rd, v_rd;        // LDS read bases of this lane
@@ -200,8 +210,8 @@ struct Wave {
   template <int KS, int VS, bool DO_S, bool DO_PV>
   __device__ __forceinline__ void mfma_phase_bf16(const char* smem) {
     using L = Lds<D, QK8>;
-    constexpr int NS = DO_S ? 2 * NDS : 0;
-    constexpr int NPV = DO_PV ? 4 * NDB : 0;
+    constexpr int NS = DO_S ? NKB * NDS : 0;
+    constexpr int NPV = DO_PV ? 2 * NKB * NDB : 0;
     constexpr int N = NS + NPV;
     constexpr int NM = NS < NPV ? NS : NPV;
     constexpr int LA = N < kLookahead ? N : kLookahead;
@@ -213,7 +223,7 @@ struct Wave {
     auto load = [&](int j) {
       const int i = idx(j);
       if (is_s(j)) {
-        const int ds = i >> 1, kb = i & 1;
+        const int ds = i / NKB, kb = i % NKB;
         fr[j] = *reinterpret_cast<const bf16x8*>(kb_ + kb * 32 * L::KP + ds * 32);
       } else {
         const int kbc = i / NDB, db = i % NDB;     // kbc = 2kb + c
@@ -221,8 +231,8 @@ struct Wave {
       }
     };
     if (DO_S) {
-      s[0] = f32x16{};
-      s[1] = f32x16{};
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
     }
 #pragma unroll
     for (int j = 0; j < LA; ++j) load(j);
@@ -231,7 +241,7 @@ struct Wave {
     for (int j = 0; j < N; ++j) {
       const int i = idx(j);
       if (is_s(j)) {
-        const int ds = i >> 1, kb = i & 1;
+        const int ds = i / NKB, kb = i % NKB;
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j], qf.v[ds], s[kb], 0, 0, 0);
       } else {
         const int kbc = i / NDB, db = i % NDB;
@@ -250,7 +260,7 @@ struct Wave {
   template <int KS, int VS, bool DO_S, bool DO_PV>
   __device__ __forceinline__ void mfma_phase_fp8(const char* smem) {
     using L = Lds<D, QK8>;
-    using Pl = Fp8Plan<DO_S ? 2 * NDS : 0, DO_PV ? 4 * NDB : 0>;
+    using Pl = Fp8Plan<DO_S ? NKB * NDS : 0, DO_PV ? 2 * NKB * NDB : 0>;
     const char* kb_ = smem + k_rd + KS * L::KTILE;
     const char* vb_ = smem + v_rd + VS * L::VTILE;
     i32x8 sf[Pl::NS > 0 ? Pl::NS : 1];
@@ -261,7 +271,7 @@ struct Wave {
         constexpr int j = Pl::unit_step(u);
         constexpr int i = Pl::idx(j);
         if constexpr (Pl::is_s(j)) {
-          constexpr int h = u - Pl::ustart(j), ds = i >> 1, kb = i & 1;
+          constexpr int h = u - Pl::ustart(j), ds = i / NKB, kb = i % NKB;
           const u32x4 x = *reinterpret_cast<const u32x4*>(kb_ + kb * 32 * L::KP + ds * 64 + 16 * h);
 #pragma unroll
           for (int e = 0; e < 4; ++e) sf[i][4 * h + e] = (int)x[e];
@@ -272,8 +282,8 @@ struct Wave {
       }
     };
     if (DO_S) {
-      s[0] = f32x16{};
-      s[1] = f32x16{};
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
     }
     static_for<0, Pl::LA>(load_unit);
     __builtin_amdgcn_sched_barrier(0);
@@ -281,7 +291,7 @@ struct Wave {
       constexpr int j = decltype(J)::value;
       constexpr int i = Pl::idx(j);
       if constexpr (Pl::is_s(j)) {
-        constexpr int ds = i >> 1, kb = i & 1;
+        constexpr int ds = i / NKB, kb = i % NKB;
         s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(sf[i], qf.v[ds], s[kb], 0, 0, 0, 127, 0, 127);
       } else {
         constexpr int kbc = i / NDB, db = i % NDB;
@@ -295,7 +305,7 @@ struct Wave {
   // Softmax phase of tile t: online softmax of S_t (exp2 domain, lazy rescale) -> P_t.
   // valid = keys of the tile inside the partition.
   __device__ __forceinline__ void softmax_phase(int valid, float c2, int half) {
-    if (valid < kBK) softmax<true>(valid, c2, half);
+    if (valid < KB) softmax<true>(valid, c2, half);
     else softmax<false>(valid, c2, half);
   }
 
@@ -309,7 +319,7 @@ struct Wave {
   __device__ __forceinline__ void softmax(int valid, float c2, int half) {
     if (MASK) {  // keys past the end of the partition
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
@@ -320,7 +330,9 @@ struct Wave {
 #pragma unroll
     for (int r = 1; r < 16; ++r) x = fmaxf(x, s[0][r]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) x = fmaxf(x, s[1][r]);
+    for (int kb = 1; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x = fmaxf(x, s[kb][r]);
     if (__builtin_amdgcn_ballot_w64(x * c2 > m + kRescaleThreshold) != 0) {
       const float mx = wave_max_halves(x) * c2;
       const float mn = fmaxf(m, mx);
@@ -338,7 +350,7 @@ struct Wave {
     // would put the bf16 unit roundoff (2^-8) straight into LSE
     float acc0 = l, acc1 = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         bf16x8 p;
@@ -357,18 +369,19 @@ struct Wave {
   }
 };
 
-// Tile staging. Group 1 (waves 4-7) owns K: 16-byte chunks, a row per 16 lanes.
-// Group 0 (waves 0-3) owns V: a unit is 4 keys x 8 d, transposed in registers and
-// written as 8-byte key groups of 8 V^T rows; the 16 lanes of a write pass cover
-// the 16 key groups of one row.
+// Tile staging. Group 1 (waves 4-7) owns K: 16-byte chunks, D / 8 (bf16) or D / 16
+// (fp8) lanes per row. Group 0 (waves 0-3) owns V: a unit is 4 keys x 8 d,
+// transposed in registers and written as 8-byte key groups of 8 V^T rows; KB / 4
+// consecutive lanes cover the key groups of one row.
 template <int D, bool QK8>
 struct Stager {
   static constexpr int KCH = QK8 ? D / 16 : D / 8;  // 16-byte chunks per K row
   static constexpr int VCH = D / 8;                 // 16-byte chunks per V row
   static constexpr int GT = kThreads / 2;           // threads per group
-  static constexpr int KLOADS = kBK * KCH / GT;     // K chunks per thread
+  static constexpr int KB = Tile<D>::KB;
+  static constexpr int KLOADS = KB * KCH / GT;      // K chunks per thread
   static constexpr int KROWS = GT / KCH;            // K rows per load round
-  static constexpr int VUNITS = (kBK / 4) * VCH;    // V units per tile
+  static constexpr int VUNITS = (KB / 4) * VCH;     // V units per tile
   static constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw 32-bit buffer, no swizzle
   u32x4 r[4];
   const char* src;       // K or V rows of this (b, h) starting at the partition
@@ -383,9 +396,9 @@ struct Stager {
   // partition's end are range-checked by the hardware and return zeros, without a
   // branch or a clamp per lane. A tile past the end gets an empty range.
   __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(int tile) const {
-    const int rows = n - tile * kBK;
-    const int bytes = rows > 0 ? (min(rows, kBK) - 1) * stride_bytes + row_bytes : 0;
-    const uint64_t base = reinterpret_cast<uint64_t>(src + (int64_t)(rows > 0 ? tile * kBK : 0) * stride_bytes);
+    const int rows = n - tile * KB;
+    const int bytes = rows > 0 ? (min(rows, KB) - 1) * stride_bytes + row_bytes : 0;
+    const uint64_t base = reinterpret_cast<uint64_t>(src + (int64_t)(rows > 0 ? tile * KB : 0) * stride_bytes);
     // all of it is wave-uniform; readfirstlane keeps the descriptor in SGPRs
     const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base);
     const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32));
@@ -502,7 +515,7 @@ void attn_bf16_kernel(const AttnArgs a) {
 #pragma unroll
   for (int db = 0; db < W::NDB; ++db) w.o[db] = f32x16{};
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < W::NKB; ++kb)
 #pragma unroll
     for (int c = 0; c < 2; ++c) w.pf[kb][c] = bf16x8{};
   w.m = -INFINITY;
@@ -511,7 +524,8 @@ void attn_bf16_kernel(const AttnArgs a) {
   w.v_rd = L::V0 + l32 * L::VP + 16 * half;
   // fp8 scores are in units of the two dequantisation factors of this (b, h)
   const float c2 = QK8 ? a.scale_log2 * a.q_scale[bh] * a.k_scale[bh] : a.scale_log2;
-  const int T = (n + kBK - 1) / kBK;
+  constexpr int KB = Tile<D>::KB;
+  const int T = (n + KB - 1) / KB;
 
   St st;
   st.n = n;
@@ -530,7 +544,7 @@ void attn_bf16_kernel(const AttnArgs a) {
     st.stride_bytes = (int)(a.k_ss * 2);
     st.row_bytes = D * 2;
     st.src = reinterpret_cast<const char*>(a.v) + kv_off * 2;
-    const int va = gtid & 15, vc = gtid >> 4;   // 4-key group, 8-wide d chunk
+    const int va = gtid % (KB / 4), vc = gtid / (KB / 4);   // 4-key group, 8-wide d chunk
 #pragma unroll
     for (int j = 0; j < 4; ++j) st.voff[j] = (4 * va + j) * st.stride_bytes + vc * 16;
     st.w_off = L::V0 + (8 * vc) * L::VP + vt_group_pos(va);
@@ -557,13 +571,13 @@ void attn_bf16_kernel(const AttnArgs a) {
     for (; t + 1 < T; t += 2) {
       w.template mfma_phase<1, 0, true, true>(smem);     // X_t, t odd
       lds_barrier();
-      w.softmax_phase(n - t * kBK, c2, half);
+      w.softmax_phase(n - t * KB, c2, half);
       if (t + 2 < T) st.template store_k<1>(smem);
       st.load_k(t + 3);
       lds_barrier();
       w.template mfma_phase<0, 1, true, true>(smem);     // X_{t+1}, even
       lds_barrier();
-      w.softmax_phase(n - (t + 1) * kBK, c2, half);
+      w.softmax_phase(n - (t + 1) * KB, c2, half);
       if (t + 3 < T) st.template store_k<0>(smem);
       st.load_k(t + 4);
       lds_barrier();
@@ -571,7 +585,7 @@ void attn_bf16_kernel(const AttnArgs a) {
     if (t < T) {  // t odd, last tile
       w.template mfma_phase<1, 0, true, true>(smem);
       lds_barrier();
-      w.softmax_phase(n - t * kBK, c2, half);
+      w.softmax_phase(n - t * KB, c2, half);
       lds_barrier();
       w.template mfma_phase<0, 1, false, true>(smem);    // X_T, V slot (T-1)&1 = 1
     } else {      // T even (or 1): V slot (T-1)&1
@@ -592,13 +606,13 @@ void attn_bf16_kernel(const AttnArgs a) {
     for (; t + 1 < T; t += 2) {
       w.template mfma_phase<1, 0, true, true>(smem);
       lds_barrier();
-      w.softmax_phase(n - t * kBK, c2, half);
+      w.softmax_phase(n - t * KB, c2, half);
       st.template store_v<1>(smem);
       st.load_v(t + 1);
       lds_barrier();
       w.template mfma_phase<0, 1, true, true>(smem);
       lds_barrier();
-      w.softmax_phase(n - (t + 1) * kBK, c2, half);
+      w.softmax_phase(n - (t + 1) * KB, c2, half);
       st.template store_v<0>(smem);
       st.load_v(t + 2);
       lds_barrier();
@@ -606,7 +620,7 @@ void attn_bf16_kernel(const AttnArgs a) {
     if (t < T) {
       w.template mfma_phase<1, 0, true, true>(smem);
       lds_barrier();
-      w.softmax_phase(n - t * kBK, c2, half);
+      w.softmax_phase(n - t * KB, c2, half);
       st.template store_v<1>(smem);
       lds_barrier();
       w.template mfma_phase<0, 1, false, true>(smem);
