@@ -364,6 +364,22 @@ def main():
             runner._timed("attn_fresh_fp8", N.partition_attn_fp8, q18, k18, v1, qs18, ks18, near_ranges, w.scale,
                           out=f_out, lse=f_lse)
 
+        # the whole step (anchor + next step, with their compositions and weights) on fp8 q/k
+        runner.timer = None
+        runner.anchor(q8, k8, v, (qs8, ks8))
+        runner.step(q18, k18, v1, (qs18, ks18))
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            runner.anchor(q8, k8, v, (qs8, ks8))
+            runner.step(q18, k18, v1, (qs18, ks18))
+        e1.record()
+        torch.cuda.synchronize()
+        fp8_step_ms = e0.elapsed_time(e1) / args.steps
+        kernels["step_fp8"] = {"ms": round(fp8_step_ms, 4), "TFLOP/s": round(step_flops / fp8_step_ms / 1e9, 1),
+                               "speedup_vs_bf16": round(ms_step / fp8_step_ms, 3)}
+
         runner.timer = None
         fp8_calls()
         torch.cuda.synchronize()

@@ -84,19 +84,30 @@ class SelectiveReuse:
         self.timer.append((name, start, end))
         return r
 
-    def anchor(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor) -> None:
-        """Step t: all partition states, their weights, and the cached composition of the far ones."""
-        self._timed("attn_anchor", _native.partition_attn, q, k, v, self.ranges, self.scale,
-                    out=self.state_out, lse=self.state_lse)
+    def _attn(self, name: str, q, k, v, ranges, out, lse, scales) -> None:
+        """Partition states: bf16 (or fp32) q/k/v, or fp8 E4M3 q/k with scales = (q_scale, k_scale)."""
+        if q.dtype == torch.float8_e4m3fn:
+            if scales is None:
+                raise ValueError("fp8 q/k need their dequantisation factors (q_scale, k_scale)")
+            self._timed(name, _native.partition_attn_fp8, q, k, v, scales[0], scales[1], ranges, self.scale,
+                        out=out, lse=lse)
+        else:
+            self._timed(name, _native.partition_attn, q, k, v, ranges, self.scale, out=out, lse=lse)
+
+    def anchor(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scales=None) -> None:
+        """Step t: all partition states, their weights, and the cached composition of the far ones.
+        q and k may be fp8 E4M3 codes, with scales = (q_scale, k_scale) float32 [B, H]."""
+        self._attn("attn_anchor", q, k, v, self.ranges, self.state_out, self.state_lse, scales)
         self._timed("contrib_anchor", self._contribution, self.state_lse, self.anchor_weights, self.anchor_scores)
         self._timed("merge_cached", _native.merge, [self.state_out[i] for i in self.far],
                     [self.state_lse[i] for i in self.far], out=self.cached_out, lse=self.cached_lse)
 
-    def step(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
-        """Step t+1: fresh near states composed with the cached state; returns (OUT, LSE)."""
+    def step(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scales=None) -> Tuple[torch.Tensor, torch.Tensor]:
+        """Step t+1: fresh near states composed with the cached state; returns (OUT, LSE).
+        q and k may be fp8 E4M3 codes, with scales = (q_scale, k_scale) float32 [B, H]."""
         nf = len(self.near)
-        self._timed("attn_fresh", _native.partition_attn, q, k, v, [self.ranges[i] for i in self.near], self.scale,
-                    out=self.step_out[:nf], lse=self.step_lse[:nf])
+        self._attn("attn_fresh", q, k, v, [self.ranges[i] for i in self.near], self.step_out[:nf],
+                   self.step_lse[:nf], scales)
         self._timed("merge_step", _native.merge, [self.step_out[j] for j in range(nf + 1)],
                     [self.step_lse[j] for j in range(nf + 1)], out=self.result_out, lse=self.result_lse)
         self._timed("contrib_step", self._contribution, self.step_lse, self.step_weights, self.step_scores)

@@ -126,6 +126,27 @@ def test_fp8_small_ragged(D, state):
     check_states(out.float(), lse, o_ref, l_ref, BF16_OUT, BF16_LSE, f"fp8 D={D} {state}")
 
 
+def test_selective_reuse_with_fp8_inputs():
+    """The reuse step on fp8 q/k: anchor states at t, 2 fresh partitions at t+1 composed with the
+    cached composition of the other 6, against the oracle's reuse step on the decoded states."""
+    ranges = inputs.equal_ranges(1024, 8)
+    w = inputs.small_case_fp8(90, 1, 2, 300, 1024, 128, ranges)
+    w1 = inputs.small_case_fp8(91, 1, 2, 300, 1024, 128, ranges)
+    near = [3, 4]
+    runner = SelectiveReuse(1, 2, 300, 128, ranges, near, DEV, w.scale)
+    note("selective reuse with fp8 q/k, P=8, 2 fresh")
+    runner.anchor(to_dev(w.q8), to_dev(w.k8), to_dev(w.v), (to_dev(w.q_scale), to_dev(w.k_scale)))
+    out, lse = runner.step(to_dev(w1.q8), to_dev(w1.k8), to_dev(w1.v), (to_dev(w1.q_scale), to_dev(w1.k_scale)))
+    torch.cuda.synchronize()
+    o_t, l_t = fp8_reference(w, w.q8, w.k8, w.q_scale, w.k_scale, ranges, w.scale)
+    o_t1, l_t1 = fp8_reference(w1, w1.q8, w1.k8, w1.q_scale, w1.k_scale, ranges, w.scale)
+    ref_out, ref_lse, c_out, c_lse = oracle.selective_reuse(o_t, l_t, o_t1, l_t1, near)
+    check_states(runner.cached_out, runner.cached_lse, c_out, c_lse, BF16_OUT, BF16_LSE, "fp8 cached state")
+    check_states(out, lse, ref_out, ref_lse, BF16_OUT, BF16_LSE, "fp8 reuse result")
+    with pytest.raises(ValueError):
+        runner.step(to_dev(w1.q8), to_dev(w1.k8), to_dev(w1.v))
+
+
 def test_fp8_path_equals_bf16_path_on_the_same_values():
     """Codes of moderate size with factors 1 are exact in bf16, so both paths score the same Q and K.
     The fp8 MFMA sums 64 products per instruction and rounds differently from four bf16 MFMAs (LSE
