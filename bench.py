@@ -283,7 +283,36 @@ def main():
         kernels[n] = {"P": P, "ms": round(ms, 4), "GB/s": round(by / ms / 1e6, 1)}
     merge_gbps = merge_bytes_total / (merge_ms_total * 1e-3) / 1e9
 
+    reuse_quality = None
     if reuse:
+        # quality of the reuse step (outside the timed region): the step's result against full
+        # attention at t+1 (all 32 partitions, composed), and the time that full attention takes
+        runner.timer = None
+        runner.anchor(q, k, v)
+        r_out, r_lse = runner.step(q1, k1, v1)
+        full_out = torch.empty_like(runner.state_out)
+        full_lse = torch.empty_like(runner.state_lse)
+        f_out = torch.empty_like(merge_out)
+        f_lse = torch.empty_like(merge_lse)
+        torch.cuda.synchronize()
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record()
+        N.partition_attn(q1, k1, v1, w.ranges, w.scale, out=full_out, lse=full_lse)
+        e1.record()
+        N.merge(list(full_out), list(full_lse), out=f_out, lse=f_lse)
+        e2.record()
+        torch.cuda.synchronize()
+        near_mass = runner.anchor_scores[:, near].sum(dim=1).mean().item()
+        fresh_ms = kernels["attn_fresh"]["ms"] + kernels["merge_step"]["ms"]
+        reuse_quality = {
+            "mse_vs_full": float(torch.mean((r_out - f_out) ** 2).item()),
+            "lse_max_abs_vs_full": float((r_lse - f_lse).abs().max().item()),
+            "near_weight_mass": round(near_mass, 4),
+            "full_attention_ms": round(e0.elapsed_time(e1) + e1.elapsed_time(e2), 4),
+            "reuse_attention_ms": round(fresh_ms, 4),
+            "attention_time_ratio": round((e0.elapsed_time(e1) + e1.elapsed_time(e2)) / fresh_ms, 2)}
+        del full_out, full_lse, f_out, f_lse
+
         # planner statistics (timed on their own, outside the step): anchor norms of every
         # partition's OUT, global weights, the local drift and the decision
         eps = torch.tensor([1e-4], dtype=torch.float32, device=dev)
@@ -435,6 +464,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "reuse_quality": reuse_quality,
     }
     print(json.dumps(line), flush=True)
 
