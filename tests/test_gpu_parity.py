@@ -70,9 +70,10 @@ def test_bf16_small_ragged(D):
     check_states(out, lse, o_ref, l_ref, BF16_OUT, BF16_LSE, f"bf16 D={D}")
 
 
-def test_bf16_strided_inputs_and_guarded_outputs():
+@pytest.mark.parametrize("D", [128, 64])
+def test_bf16_strided_inputs_and_guarded_outputs(D):
     """Non-contiguous q/k/v views and outputs followed by canaries that must stay untouched."""
-    D, B, H, Sq, Skv = 128, 1, 2, 130, 333
+    B, H, Sq, Skv = 1, 2, 130, 333
     w = inputs.small_case(21, B, H, Sq, Skv, D, [(0, 333), (5, 70), (300, 333)])
     qbig = torch.zeros(B, H, Sq + 16, D + 64, dtype=torch.bfloat16)
     qbig[:, :, 8:8 + Sq, :D] = w.q
@@ -86,7 +87,7 @@ def test_bf16_strided_inputs_and_guarded_outputs():
     guard = 4096
     obuf = torch.full((n_out + guard,), 12345.0, device=DEV)
     lbuf = torch.full((n_lse + guard,), 12345.0, device=DEV)
-    note("bf16 strided views + guarded outputs")
+    note(f"bf16 strided views + guarded outputs D={D}")
     out, lse = N.partition_attn(qd, kd, vd, w.ranges, w.scale, out=obuf[:n_out].view(P, B, H, Sq, D),
                                 lse=lbuf[:n_lse].view(P, B, H, Sq))
     torch.cuda.synchronize()
@@ -164,6 +165,18 @@ def test_fp8_path_equals_bf16_path_on_the_same_values():
     torch.cuda.synchronize()
     assert (l8 - l16).abs().max().item() <= BF16_LSE
     assert (o8 - o16).abs().max().item() <= 1e-2
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_fp8_large_logits_stay_finite(D):
+    """fp8 q/k with the softmax scale x100 (very peaked, several lazy rescales): finite and at parity."""
+    w = inputs.small_case_fp8(33 + D, 1, 2, 64, 500, D, [(0, 500), (0, 17), (250, 500)])
+    note(f"fp8 large logits D={D}")
+    out, lse = N.partition_attn_fp8(to_dev(w.q8), to_dev(w.k8), to_dev(w.v), to_dev(w.q_scale), to_dev(w.k_scale),
+                                    w.ranges, 100 * w.scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = fp8_reference(w, w.q8, w.k8, w.q_scale, w.k_scale, w.ranges, 100 * w.scale)
+    check_states(out, lse, o_ref, l_ref, BF16_OUT, 1e-3 * 100, f"fp8 x100 logits D={D}")
 
 
 def test_fp8_strided_inputs_and_guarded_outputs():
