@@ -318,13 +318,15 @@ struct Wave {
   template <bool MASK>
   __device__ __forceinline__ void softmax(int valid, float c2, int half) {
     if (MASK) {  // keys past the end of the partition
+      // key = kb * 32 + 8 (r / 4) + 4 half + r % 4 >= valid, with the lane part moved to
+      // the right: every comparison is an immediate against one register (per-key
+      // indices would be hoisted out of the tile loop and held in ~30 VGPRs)
+      const int lim = valid - 4 * half;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (key >= valid) s[kb][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s[kb][r] = -INFINITY;
     }
     float x = s[0][0];
 #pragma unroll
