@@ -552,6 +552,16 @@ void attn_bf16_kernel(const AttnArgs a) {
     st.w_off = L::V0 + (8 * vc) * L::VP + vt_group_pos(va);
     st.on = gtid < St::VUNITS;
   }
+  // wave-uniform: the per-tile descriptor arithmetic then runs on the scalar unit
+  {
+    const uint64_t p = reinterpret_cast<uint64_t>(st.src);
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
+    st.src = reinterpret_cast<const char*>(lo | (hi << 32));
+    st.stride_bytes = __builtin_amdgcn_readfirstlane(st.stride_bytes);
+    st.row_bytes = __builtin_amdgcn_readfirstlane(st.row_bytes);
+    st.n = __builtin_amdgcn_readfirstlane(st.n);
+  }
 
   // Both groups pass 2T + 3 barriers: group 1's extra leading phase (staging
   // K tile 1) is matched by group 0's trailing empty phase.
