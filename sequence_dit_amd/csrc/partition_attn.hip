@@ -563,86 +563,97 @@ void attn_bf16_kernel(const AttnArgs a) {
     st.n = __builtin_amdgcn_readfirstlane(st.n);
   }
 
-  // Both groups pass 2T + 3 barriers: group 1's extra leading phase (staging
-  // K tile 1) is matched by group 0's trailing empty phase.
-  if (grp == 1) {
-    st.load_k(0);
-    st.template store_k<0>(smem);
-    st.load_k(1);
-    lds_barrier();                                   // K tile 0 visible
-    if (T > 1) st.template store_k<1>(smem);         // phase Y_{-1}
-    st.load_k(2);
-    lds_barrier();
-    w.template mfma_phase<0, 0, true, false>(smem);  // X_0
-    lds_barrier();
-    w.softmax_phase(n, c2, half);                    // Y_0
-    if (T > 2) st.template store_k<0>(smem);
-    st.load_k(3);
-    lds_barrier();
-    int t = 1;
-    for (; t + 1 < T; t += 2) {
-      w.template mfma_phase<1, 0, true, true>(smem);     // X_t, t odd
+  // The schedule; ON = false is the copy for a wave whose 32 rows all lie past Sq
+  // (last query tile): it only stages and passes the same barriers.
+  auto schedule = [&](auto ONC) {
+    constexpr bool ON = decltype(ONC)::value;
+    // Both groups pass 2T + 3 barriers: group 1's extra leading phase (staging
+    // K tile 1) is matched by group 0's trailing empty phase.
+    if (grp == 1) {
+      st.load_k(0);
+      st.template store_k<0>(smem);
+      st.load_k(1);
+      lds_barrier();                                   // K tile 0 visible
+      if (T > 1) st.template store_k<1>(smem);         // phase Y_{-1}
+      st.load_k(2);
       lds_barrier();
-      w.softmax_phase(n - t * KB, c2, half);
-      if (t + 2 < T) st.template store_k<1>(smem);
-      st.load_k(t + 3);
+      if constexpr (ON) w.template mfma_phase<0, 0, true, false>(smem);  // X_0
       lds_barrier();
-      w.template mfma_phase<0, 1, true, true>(smem);     // X_{t+1}, even
+      if constexpr (ON) w.softmax_phase(n, c2, half);                    // Y_0
+      if (T > 2) st.template store_k<0>(smem);
+      st.load_k(3);
       lds_barrier();
-      w.softmax_phase(n - (t + 1) * KB, c2, half);
-      if (t + 3 < T) st.template store_k<0>(smem);
-      st.load_k(t + 4);
+      int t = 1;
+      for (; t + 1 < T; t += 2) {
+        if constexpr (ON) w.template mfma_phase<1, 0, true, true>(smem);     // X_t, t odd
+        lds_barrier();
+        if constexpr (ON) w.softmax_phase(n - t * KB, c2, half);
+        if (t + 2 < T) st.template store_k<1>(smem);
+        st.load_k(t + 3);
+        lds_barrier();
+        if constexpr (ON) w.template mfma_phase<0, 1, true, true>(smem);     // X_{t+1}, even
+        lds_barrier();
+        if constexpr (ON) w.softmax_phase(n - (t + 1) * KB, c2, half);
+        if (t + 3 < T) st.template store_k<0>(smem);
+        st.load_k(t + 4);
+        lds_barrier();
+      }
+      if (t < T) {  // t odd, last tile
+        if constexpr (ON) w.template mfma_phase<1, 0, true, true>(smem);
+        lds_barrier();
+        if constexpr (ON) w.softmax_phase(n - t * KB, c2, half);
+        lds_barrier();
+        if constexpr (ON) w.template mfma_phase<0, 1, false, true>(smem);    // X_T, V slot (T-1)&1 = 1
+      } else {      // T even (or 1): V slot (T-1)&1
+        if constexpr (ON) {
+          if (T & 1) w.template mfma_phase<0, 0, false, true>(smem);
+          else w.template mfma_phase<0, 1, false, true>(smem);
+        }
+      }
       lds_barrier();
-    }
-    if (t < T) {  // t odd, last tile
-      w.template mfma_phase<1, 0, true, true>(smem);
-      lds_barrier();
-      w.softmax_phase(n - t * KB, c2, half);
-      lds_barrier();
-      w.template mfma_phase<0, 1, false, true>(smem);    // X_T, V slot (T-1)&1 = 1
-    } else {      // T even (or 1): V slot (T-1)&1
-      if (T & 1) w.template mfma_phase<0, 0, false, true>(smem);
-      else w.template mfma_phase<0, 1, false, true>(smem);
-    }
-    lds_barrier();
-  } else {
-    st.load_v(0);
-    lds_barrier();
-    w.template mfma_phase<0, 0, true, false>(smem);  // X_0
-    lds_barrier();
-    w.softmax_phase(n, c2, half);                    // Y_0
-    st.template store_v<0>(smem);
-    st.load_v(1);
-    lds_barrier();
-    int t = 1;
-    for (; t + 1 < T; t += 2) {
-      w.template mfma_phase<1, 0, true, true>(smem);
-      lds_barrier();
-      w.softmax_phase(n - t * KB, c2, half);
-      st.template store_v<1>(smem);
-      st.load_v(t + 1);
-      lds_barrier();
-      w.template mfma_phase<0, 1, true, true>(smem);
-      lds_barrier();
-      w.softmax_phase(n - (t + 1) * KB, c2, half);
-      st.template store_v<0>(smem);
-      st.load_v(t + 2);
-      lds_barrier();
-    }
-    if (t < T) {
-      w.template mfma_phase<1, 0, true, true>(smem);
-      lds_barrier();
-      w.softmax_phase(n - t * KB, c2, half);
-      st.template store_v<1>(smem);
-      lds_barrier();
-      w.template mfma_phase<0, 1, false, true>(smem);
     } else {
-      if (T & 1) w.template mfma_phase<0, 0, false, true>(smem);
-      else w.template mfma_phase<0, 1, false, true>(smem);
+      st.load_v(0);
+      lds_barrier();
+      if constexpr (ON) w.template mfma_phase<0, 0, true, false>(smem);  // X_0
+      lds_barrier();
+      if constexpr (ON) w.softmax_phase(n, c2, half);                    // Y_0
+      st.template store_v<0>(smem);
+      st.load_v(1);
+      lds_barrier();
+      int t = 1;
+      for (; t + 1 < T; t += 2) {
+        if constexpr (ON) w.template mfma_phase<1, 0, true, true>(smem);
+        lds_barrier();
+        if constexpr (ON) w.softmax_phase(n - t * KB, c2, half);
+        st.template store_v<1>(smem);
+        st.load_v(t + 1);
+        lds_barrier();
+        if constexpr (ON) w.template mfma_phase<0, 1, true, true>(smem);
+        lds_barrier();
+        if constexpr (ON) w.softmax_phase(n - (t + 1) * KB, c2, half);
+        st.template store_v<0>(smem);
+        st.load_v(t + 2);
+        lds_barrier();
+      }
+      if (t < T) {
+        if constexpr (ON) w.template mfma_phase<1, 0, true, true>(smem);
+        lds_barrier();
+        if constexpr (ON) w.softmax_phase(n - t * KB, c2, half);
+        st.template store_v<1>(smem);
+        lds_barrier();
+        if constexpr (ON) w.template mfma_phase<0, 1, false, true>(smem);
+      } else {
+        if constexpr (ON) {
+          if (T & 1) w.template mfma_phase<0, 0, false, true>(smem);
+          else w.template mfma_phase<0, 1, false, true>(smem);
+        }
+      }
+      lds_barrier();
+      lds_barrier();   // group 1's trailing X_T phase
     }
-    lds_barrier();
-    lds_barrier();   // group 1's trailing X_T phase
-  }
+  };
+  if (__builtin_amdgcn_readfirstlane(q0 + wave * kRowsPerWave) < a.Sq) schedule(std::true_type{});
+  else schedule(std::false_type{});
 
   // ---- epilogue: OUT = O / l, LSE = (m + log2 l) ln 2
   const float lt = wave_sum_halves(w.l);
