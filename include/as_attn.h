@@ -24,7 +24,9 @@
  *     shape returns AS_ERR_UNSUPPORTED; in both cases nothing is enqueued.
  *     A failed launch returns AS_ERR_HIP. as_last_error() gives the detail.
  *     Nothing throws across the ABI.
- *   - Aliasing: outputs must not overlap inputs.
+ *   - Aliasing: outputs must not overlap inputs or one another. Every call checks
+ *     the byte ranges its arguments span (for strided tensors, first to last
+ *     element) and returns AS_ERR_INVALID_ARG on an overlap.
  *   - Floating point: inputs must be finite (NaN/Inf inputs give undefined
  *     results); -inf in an LSE input marks an empty state.
  */
@@ -70,11 +72,15 @@ typedef enum {
  * dtype      AS_BF16: D must be 64 or 128. AS_F32: D a multiple of 4, 4..128.
  * kv_ranges  HOST int32 [P][2] = {s_i, e_i} with 0 <= s_i <= e_i <= Skv. Ranges may
  *            overlap, repeat or be empty. 0 <= P <= AS_MAX_PARTITIONS.
- * scale      softmax scale (callers pass 1/sqrt(D) for standard attention); finite.
+ * scale      softmax scale (callers pass 1/sqrt(D) for standard attention); finite and
+ *            >= 0. scale = 0 weighs every key of a range equally: OUT_i = mean of V over
+ *            the range, LSE_i = log(n_i).
  * out        DEVICE float32 [P][B][H][Sq][D], contiguous, 16-byte aligned.
  * lse        DEVICE float32 [P][B][H][Sq], contiguous, 4-byte aligned.
+ *            out and lse must not overlap each other or q, k, v (checked).
  * Alignment: q, k, v 16-byte aligned; strides multiples of 8 elements (bf16) or
- * 4 elements (f32); stride_s >= D. B*H <= 65535; a range spans < 2^31 bytes.
+ * 4 elements (f32); stride_s >= D. B*H <= 65535; max(n_i, 128) * kv_stride[2] *
+ * element size < 2^31 bytes for every range (else AS_ERR_UNSUPPORTED).
  * If B*H*Sq == 0 or P == 0 nothing is enqueued and AS_OK is returned.
  */
 as_status as_partition_attn(const void* q, const void* k, const void* v, as_dtype dtype,
@@ -98,7 +104,8 @@ as_status as_partition_attn(const void* q, const void* k, const void* v, as_dtyp
  * outs       HOST array of n DEVICE pointers, each float32 [rows][D] contiguous, 16-byte aligned.
  * lses       HOST array of n DEVICE pointers, each float32 [rows].
  * rows, D    rows >= 0; D a multiple of 4, 4 <= D <= 1024.
- * out, lse   DEVICE float32 [rows][D] (16-byte aligned) and [rows]; must not overlap any input.
+ * out, lse   DEVICE float32 [rows][D] (16-byte aligned) and [rows]; must not overlap any
+ *            input or each other (byte ranges checked).
  * If rows == 0 nothing is enqueued.
  */
 as_status as_merge(int32_t n, const float* const* outs, const float* const* lses,
@@ -143,8 +150,9 @@ as_status as_partition_attn_states(const void* q, const void* k, const void* v, 
  * S = K Q^T runs on the fp8 MFMA (exact products, fp32 accumulation); softmax, P and
  * PV are as in the bf16 path.
  *
- * q_scale, k_scale  DEVICE float32 [B*H], 4-byte aligned; values must be finite and
- *                   positive (not checked: they are device memory).
+ * q_scale, k_scale  DEVICE float32 [B*H], 4-byte aligned; values must be finite (not
+ *                   checked: they are device memory). Any sign is allowed: a zero
+ *                   factor weighs the keys equally, as scale = 0 does.
  * q_stride          element (= byte) strides of q over (b, h, s).
  * kv_stride         element strides of k and v over (b, h, s): k's row stride is
  *                   kv_stride[2] bytes, v's 2 * kv_stride[2] bytes. All strides are

@@ -115,10 +115,38 @@ def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def _require_gpu(*ts: torch.Tensor) -> None:
+def _require_gpu(*ts: Optional[torch.Tensor]) -> None:
+    """Every tensor whose pointer reaches the library lives on one HIP device (None is skipped)."""
+    dev = None
     for t in ts:
+        if t is None:
+            continue
         if not t.is_cuda:
             raise ValueError("tensors must live on a HIP device; the library has no CPU path")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"tensors must live on one device (found {dev} and {t.device})")
+
+
+def _check_buf(t: torch.Tensor, name: str, dtype: torch.dtype, numel: int) -> None:
+    """A caller-supplied buffer the library reads or writes as `numel` contiguous elements of `dtype`."""
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements, has {t.numel()}")
+
+
+def _check_workspace(t: torch.Tensor, need: int) -> int:
+    """A caller-supplied workspace of at least `need` bytes; returns its size in bytes."""
+    if not t.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    nbytes = t.numel() * t.element_size()
+    if nbytes < need:
+        raise ValueError(f"workspace of {nbytes} bytes is smaller than the {need} bytes needed")
+    return nbytes
 
 
 def _i64(vals) -> ctypes.Array:
@@ -164,7 +192,6 @@ def partition_attn_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_scal
     [B,H,Skv,D]) with float32 dequantisation factors q_scale, k_scale [B,H] (a code c of
     (b, h) stands for c * scale[b, h]) and bfloat16 values v (same shape and strides as k).
     Returns OUT [P,B,H,Sq,D] of state_dtype and LSE [P,B,H,Sq] float32."""
-    _require_gpu(q, k, v, q_scale, k_scale)
     fp8 = torch.float8_e4m3fn
     if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or k.stride() != v.stride():
         raise ValueError("q must be [B,H,Sq,D]; k and v [B,H,Skv,D] with equal strides")
@@ -181,14 +208,8 @@ def partition_attn_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_scal
     Skv = k.shape[2]
     P = len(kv_ranges)
     code = _state_code(state_dtype)
-    if out is None:
-        out = torch.empty((P, B, H, Sq, D), dtype=state_dtype, device=q.device)
-    if lse is None:
-        lse = torch.empty((P, B, H, Sq), dtype=torch.float32, device=q.device)
-    if not (out.is_contiguous() and lse.is_contiguous() and out.dtype == state_dtype and lse.dtype == torch.float32):
-        raise ValueError("out must be contiguous of the state dtype and lse contiguous float32")
-    if out.numel() != P * B * H * Sq * D or lse.numel() != P * B * H * Sq:
-        raise ValueError("out/lse have the wrong size")
+    out, lse = _state_outputs(q, P, B, H, Sq, D, state_dtype, out, lse)
+    _require_gpu(q, k, v, q_scale, k_scale, out, lse)
     flat = [int(x) for r in kv_ranges for x in r]
     ranges = (ctypes.c_int32 * max(1, len(flat)))(*flat)
     sc = float(D ** -0.5 if scale is None else scale)
@@ -199,8 +220,18 @@ def partition_attn_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_scal
     return out, lse
 
 
+def _state_outputs(q, P, B, H, Sq, D, state_dtype, out, lse):
+    """OUT [P,B,H,Sq,D] of state_dtype and LSE [P,B,H,Sq] float32: allocated, or the caller's checked."""
+    if out is None:
+        out = torch.empty((P, B, H, Sq, D), dtype=state_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((P, B, H, Sq), dtype=torch.float32, device=q.device)
+    _check_buf(out, "out", state_dtype, P * B * H * Sq * D)
+    _check_buf(lse, "lse", torch.float32, P * B * H * Sq)
+    return out, lse
+
+
 def _attn(q, k, v, kv_ranges, scale, out, lse, state_dtype):
-    _require_gpu(q, k, v)
     if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or k.stride() != v.stride():
         raise ValueError("q must be [B,H,Sq,D]; k and v [B,H,Skv,D] with equal strides")
     if q.dtype != k.dtype or k.dtype != v.dtype or q.dtype not in (torch.bfloat16, torch.float32):
@@ -214,14 +245,8 @@ def _attn(q, k, v, kv_ranges, scale, out, lse, state_dtype):
     P = len(kv_ranges)
     odt = torch.float32 if state_dtype is None else state_dtype
     code = _state_code(odt)
-    if out is None:
-        out = torch.empty((P, B, H, Sq, D), dtype=odt, device=q.device)
-    if lse is None:
-        lse = torch.empty((P, B, H, Sq), dtype=torch.float32, device=q.device)
-    if not (out.is_contiguous() and lse.is_contiguous() and out.dtype == odt and lse.dtype == torch.float32):
-        raise ValueError("out must be contiguous of the state dtype and lse contiguous float32")
-    if out.numel() != P * B * H * Sq * D or lse.numel() != P * B * H * Sq:
-        raise ValueError("out/lse have the wrong size")
+    out, lse = _state_outputs(q, P, B, H, Sq, D, odt, out, lse)
+    _require_gpu(q, k, v, out, lse)
     flat = [int(x) for r in kv_ranges for x in r]
     ranges = (ctypes.c_int32 * max(1, len(flat)))(*flat)
     dt = AS_BF16 if q.dtype == torch.bfloat16 else AS_F32
@@ -245,18 +270,18 @@ def merge(outs: Sequence[torch.Tensor], lses: Sequence[torch.Tensor], out: Optio
     n = len(outs)
     if n != len(lses) or n == 0:
         raise ValueError("need the same positive number of OUT and LSE tensors")
-    _require_gpu(*outs, *lses)
     D = outs[0].shape[-1]
     rows = outs[0].numel() // D
     for o, l in zip(outs, lses):
-        if o.dtype != torch.float32 or l.dtype != torch.float32 or not o.is_contiguous() or not l.is_contiguous():
-            raise ValueError("states must be contiguous float32")
-        if o.numel() != rows * D or l.numel() != rows:
-            raise ValueError("states disagree in size")
+        _check_buf(o, "a state's OUT", torch.float32, rows * D)
+        _check_buf(l, "a state's LSE", torch.float32, rows)
     if out is None:
         out = torch.empty(outs[0].shape, dtype=torch.float32, device=outs[0].device)
     if lse is None:
         lse = torch.empty(lses[0].shape, dtype=torch.float32, device=outs[0].device)
+    _check_buf(out, "out", torch.float32, rows * D)
+    _check_buf(lse, "lse", torch.float32, rows)
+    _require_gpu(*outs, *lses, out, lse)
     optrs = (ctypes.c_void_p * n)(*[o.data_ptr() for o in outs])
     lptrs = (ctypes.c_void_p * n)(*[l.data_ptr() for l in lses])
     check(lib().as_merge(n, optrs, lptrs, rows, D, out.data_ptr(), lse.data_ptr(), _stream(outs[0])))
@@ -269,20 +294,20 @@ def merge_states(outs: Sequence[torch.Tensor], lses: Sequence[torch.Tensor], out
     n = len(outs)
     if n != len(lses) or n == 0:
         raise ValueError("need the same positive number of OUT and LSE tensors")
-    _require_gpu(*outs, *lses)
     in_dtype = outs[0].dtype
     in_code, out_code = _state_code(in_dtype), _state_code(out_dtype)
     D = outs[0].shape[-1]
     rows = outs[0].numel() // D
     for o, l in zip(outs, lses):
-        if o.dtype != in_dtype or l.dtype != torch.float32 or not o.is_contiguous() or not l.is_contiguous():
-            raise ValueError("states must be contiguous, OUT of one dtype, LSE float32")
-        if o.numel() != rows * D or l.numel() != rows:
-            raise ValueError("states disagree in size")
+        _check_buf(o, "a state's OUT", in_dtype, rows * D)
+        _check_buf(l, "a state's LSE", torch.float32, rows)
     if out is None:
         out = torch.empty(outs[0].shape, dtype=out_dtype, device=outs[0].device)
     if lse is None:
         lse = torch.empty(lses[0].shape, dtype=torch.float32, device=outs[0].device)
+    _check_buf(out, "out", out_dtype, rows * D)
+    _check_buf(lse, "lse", torch.float32, rows)
+    _require_gpu(*outs, *lses, out, lse)
     optrs = (ctypes.c_void_p * n)(*[o.data_ptr() for o in outs])
     lptrs = (ctypes.c_void_p * n)(*[l.data_ptr() for l in lses])
     check(lib().as_merge_states(n, optrs, lptrs, in_code, rows, D, out_code, out.data_ptr(), lse.data_ptr(),
@@ -294,21 +319,23 @@ def compose_groups(outs: torch.Tensor, lses: torch.Tensor, group: int, out_dtype
                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
     """Group-wise composition of a partition-major block of states OUT [P, ..., D], LSE [P, ...]:
     one state per group of `group` consecutive partitions ([G, ..., D], [G, ...])."""
-    _require_gpu(outs, lses)
-    if not outs.is_contiguous() or not lses.is_contiguous() or lses.dtype != torch.float32:
-        raise ValueError("states must be contiguous with float32 LSE")
     in_code = _state_code(outs.dtype)
     out_dtype = outs.dtype if out_dtype is None else out_dtype
     out_code = _state_code(out_dtype)
     P, D = outs.shape[0], outs.shape[-1]
     rows = outs.numel() // max(P * D, 1)
-    if lses.shape[0] != P or lses.numel() != P * rows:
+    _check_buf(outs, "outs", outs.dtype, P * rows * D)
+    if lses.dim() < 1 or lses.shape[0] != P:
         raise ValueError("OUT and LSE blocks disagree")
+    _check_buf(lses, "lses", torch.float32, P * rows)
     G = (P + group - 1) // max(group, 1)
     if out is None:
         out = torch.empty((G,) + tuple(outs.shape[1:]), dtype=out_dtype, device=outs.device)
     if lse is None:
         lse = torch.empty((G,) + tuple(lses.shape[1:]), dtype=torch.float32, device=outs.device)
+    _check_buf(out, "out", out_dtype, G * rows * D)
+    _check_buf(lse, "lse", torch.float32, G * rows)
+    _require_gpu(outs, lses, out, lse)
     check(lib().as_compose_groups(outs.data_ptr(), lses.data_ptr(), in_code, P, rows, D, group, out_code,
                                   out.data_ptr(), lse.data_ptr(), _stream(outs)))
     return out, lse
@@ -325,11 +352,11 @@ def contribution_workspace_size(P: int, rows: int, rows_per_group: int) -> int:
 def partition_contribution(lse: torch.Tensor, rows_per_group: int, want_weights: bool = True,
                            want_scores: bool = True, workspace: Optional[torch.Tensor] = None):
     """Per-row weights w [P, rows] and per-group scores [rows/rows_per_group, P] from LSE [P, ...]."""
-    _require_gpu(lse)
-    if lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32")
+    if lse.dim() < 1:
+        raise ValueError("lse must be [P, ...]")
     P = lse.shape[0]
     rows = lse.numel() // max(P, 1)
+    _check_buf(lse, "lse", torch.float32, P * rows)
     w = torch.empty((P, rows), dtype=torch.float32, device=lse.device) if want_weights else None
     s = None
     ws_bytes = 0
@@ -337,10 +364,13 @@ def partition_contribution(lse: torch.Tensor, rows_per_group: int, want_weights:
         if rows_per_group < 1 or rows % rows_per_group:
             raise ValueError("rows_per_group must divide the number of rows")
         s = torch.empty((rows // rows_per_group, P), dtype=torch.float32, device=lse.device)
-        ws_bytes = contribution_workspace_size(P, rows, rows_per_group)
-        if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
-            workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=lse.device)
-        ws_bytes = workspace.numel() * workspace.element_size()
+        need = contribution_workspace_size(P, rows, rows_per_group)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=lse.device)
+        ws_bytes = _check_workspace(workspace, need)
+    else:
+        workspace = None
+    _require_gpu(lse, w, s, workspace)
     check(lib().as_partition_contribution(lse.data_ptr(), P, rows, rows_per_group,
                                           w.data_ptr() if w is not None else None,
                                           s.data_ptr() if s is not None else None,
@@ -364,32 +394,36 @@ def _ptr(t: Optional[torch.Tensor]):
 def state_norms(a: torch.Tensor, b: Optional[torch.Tensor] = None, norms: Optional[torch.Tensor] = None,
                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """||a_i|| (or ||a_i - b_i||) for every slice i of a [P, ...] float32; returns norms [P] float32."""
-    _require_gpu(a, *([b] if b is not None else []))
-    if a.dtype != torch.float32 or not a.is_contiguous() or a.dim() < 1:
-        raise ValueError("a must be a contiguous float32 tensor [P, ...]")
-    if b is not None and (b.dtype != torch.float32 or not b.is_contiguous() or b.shape != a.shape):
-        raise ValueError("b must be a contiguous float32 tensor shaped like a")
+    if a.dim() < 1:
+        raise ValueError("a must be a tensor [P, ...]")
     P = a.shape[0]
     n = a.numel() // max(P, 1)
+    _check_buf(a, "a", torch.float32, P * n)
+    if b is not None:
+        if b.shape != a.shape:
+            raise ValueError("b must be shaped like a")
+        _check_buf(b, "b", torch.float32, P * n)
     if norms is None:
         norms = torch.empty(P, dtype=torch.float32, device=a.device)
+    _check_buf(norms, "norms", torch.float32, P)
     need = state_norms_workspace_size(P, n)
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
+    if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=a.device)
+    ws_bytes = _check_workspace(workspace, need)
+    _require_gpu(a, b, norms, workspace)
     check(lib().as_state_norms(a.data_ptr(), _ptr(b), P, n, norms.data_ptr(), workspace.data_ptr(),
-                               workspace.numel() * workspace.element_size(), _stream(a)))
+                               ws_bytes, _stream(a)))
     return norms
 
 
 def planner_decide(anchor_norms: torch.Tensor, local_drift: torch.Tensor, weights: torch.Tensor,
                    eps: torch.Tensor, local: int, group: int, eps_local: float, want_stats: bool = True) -> dict:
     """One planning step (alpha, delta, group errors, compute flags, anchor flag), on the device."""
-    _require_gpu(anchor_norms, local_drift, weights, eps)
-    for t in (anchor_norms, local_drift, weights, eps):
-        if t.dtype != torch.float32 or not t.is_contiguous():
-            raise ValueError("planner inputs must be contiguous float32")
     P = anchor_norms.numel()
-    G = (P + group - 1) // max(group, 1)
+    for t, name, numel in ((anchor_norms, "anchor_norms", P), (local_drift, "local_drift", 1),
+                           (weights, "weights", P), (eps, "eps", 1)):
+        _check_buf(t, name, torch.float32, numel)
+    G = (P + min(group, P) - 1) // max(min(group, P), 1)
     dev = anchor_norms.device
     r = {"compute": torch.empty(max(G, 1), dtype=torch.int32, device=dev),
          "anchor": torch.empty(1, dtype=torch.int32, device=dev)}
@@ -397,6 +431,7 @@ def planner_decide(anchor_norms: torch.Tensor, local_drift: torch.Tensor, weight
         r["alpha"] = torch.empty(P, dtype=torch.float32, device=dev)
         r["delta"] = torch.empty(P, dtype=torch.float32, device=dev)
         r["ase"] = torch.empty(max(G, 1), dtype=torch.float32, device=dev)
+    _require_gpu(anchor_norms, local_drift, weights, eps, *r.values())
     check(lib().as_planner_decide(anchor_norms.data_ptr(), local_drift.data_ptr(), weights.data_ptr(),
                                   eps.data_ptr(), P, local, group, float(eps_local), _ptr(r.get("alpha")),
                                   _ptr(r.get("delta")), _ptr(r.get("ase")), r["compute"].data_ptr(),
@@ -407,12 +442,13 @@ def planner_decide(anchor_norms: torch.Tensor, local_drift: torch.Tensor, weight
 def planner_epsilon(corr_norms: torch.Tensor, weights: torch.Tensor, local: int, group: int,
                     reuse_fraction: float, eps: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Reuse threshold of the anchor step from per-partition correction norms; returns eps [1]."""
-    _require_gpu(corr_norms, weights)
-    for t in (corr_norms, weights):
-        if t.dtype != torch.float32 or not t.is_contiguous():
-            raise ValueError("planner inputs must be contiguous float32")
+    P = corr_norms.numel()
+    _check_buf(corr_norms, "corr_norms", torch.float32, P)
+    _check_buf(weights, "weights", torch.float32, P)
     if eps is None:
         eps = torch.empty(1, dtype=torch.float32, device=corr_norms.device)
+    _check_buf(eps, "eps", torch.float32, 1)
+    _require_gpu(corr_norms, weights, eps)
     check(lib().as_planner_epsilon(corr_norms.data_ptr(), weights.data_ptr(), corr_norms.numel(), local, group,
                                    float(reuse_fraction), eps.data_ptr(), _stream(corr_norms)))
     return eps

@@ -33,6 +33,36 @@ as_status hip_status(hipError_t e, const char* what) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Byte ranges [a, a + na) and [b, b + nb) share at least one byte.
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+// Product of non-negative sizes, or -1 when it does not fit in int64.
+int64_t mul3(int64_t a, int64_t b, int64_t c = 1) {
+  int64_t r;
+  if (__builtin_mul_overflow(a, b, &r) || __builtin_mul_overflow(r, c, &r)) return -1;
+  return r;
+}
+
+// Bytes from the first to one past the last element of a [n0][n1][n2][D] tensor with
+// element strides s[0..2] (unit stride on the last dimension), or -1 on overflow.
+// Every n >= 1.
+int64_t extent_bytes(int64_t n0, int64_t n1, int64_t n2, int64_t D, const int64_t s[3], int64_t esz) {
+  int64_t t0, t1, t2, r;
+  if (__builtin_mul_overflow(n0 - 1, s[0], &t0) || __builtin_mul_overflow(n1 - 1, s[1], &t1) ||
+      __builtin_mul_overflow(n2 - 1, s[2], &t2) || __builtin_add_overflow(t0, t1, &r) ||
+      __builtin_add_overflow(r, t2, &r) || __builtin_add_overflow(r, D, &r) || __builtin_mul_overflow(r, esz, &r))
+    return -1;
+  return r;
+}
+
+// Sizes accepted for a state block (rows * D elements): far beyond any device memory,
+// small enough that byte counts never overflow.
+constexpr int64_t kMaxRows = (int64_t)1 << 40;
+
 }  // namespace
 
 extern "C" {
@@ -76,8 +106,10 @@ as_status attn_impl(const void* q, const void* k, const void* v, as_dtype dtype,
     return fail(AS_ERR_UNSUPPORTED, "%s path supports D in {64, 128}, got %lld", qk_fp8 ? "fp8" : "bf16", (long long)D);
   if (dtype == AS_F32 && (D % 4 != 0 || D > 128))
     return fail(AS_ERR_UNSUPPORTED, "f32 path supports D a multiple of 4 up to 128, got %lld", (long long)D);
+  if (B == 0 || H == 0 || Sq == 0 || P == 0) return ok();
+  if (B > 65535 || H > 65535 || B * H > 65535) return fail(AS_ERR_UNSUPPORTED, "B*H=%lld exceeds 65535", (long long)mul3(B, H));
+  if (Sq > 0x7fffffff || Skv > 0x7fffffff) return fail(AS_ERR_UNSUPPORTED, "sequence length exceeds 2^31-1");
   const int64_t rows = B * H * Sq;
-  if (rows == 0 || P == 0) return ok();
   if (!q || !k || !v || !out || !lse) return fail(AS_ERR_INVALID_ARG, "NULL tensor pointer");
   if (!q_stride || !kv_stride) return fail(AS_ERR_INVALID_ARG, "NULL stride array");
   if (qk_fp8 && (!q_scale || !k_scale)) return fail(AS_ERR_INVALID_ARG, "q_scale and k_scale must not be NULL");
@@ -94,12 +126,30 @@ as_status attn_impl(const void* q, const void* k, const void* v, as_dtype dtype,
   if (q_stride[2] < D || kv_stride[2] < D) return fail(AS_ERR_INVALID_ARG, "sequence stride smaller than D");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16)) return fail(AS_ERR_INVALID_ARG, "q, k and v must be 16-byte aligned");
   if (!aligned(out, 16) || !aligned(lse, 4)) return fail(AS_ERR_INVALID_ARG, "out must be 16-byte and lse 4-byte aligned");
-  if (B * H > 65535) return fail(AS_ERR_UNSUPPORTED, "B*H=%lld exceeds 65535", (long long)(B * H));
-  if (Sq > 0x7fffffff || Skv > 0x7fffffff) return fail(AS_ERR_UNSUPPORTED, "sequence length exceeds 2^31-1");
+  // The bf16/fp8 kernels address the rows of a key tile (up to 128 keys, also past a
+  // shorter range's end) with 32-bit byte offsets from the tile's first row.
   for (int32_t i = 0; i < P; ++i) {
     const int64_t n = (int64_t)kv_ranges[2 * i + 1] - kv_ranges[2 * i];
-    if (n * kv_stride[2] * esz >= ((int64_t)1 << 31)) return fail(AS_ERR_UNSUPPORTED, "kv range %d spans 2^31 bytes or more", i);
+    const int64_t span = mul3(n > 128 ? n : 128, kv_stride[2], esz);
+    if (span < 0 || span >= ((int64_t)1 << 31))
+      return fail(AS_ERR_UNSUPPORTED, "kv range %d spans 2^31 bytes or more", i);
   }
+  // Outputs must not overlap each other or any byte an input may occupy.
+  const int64_t qesz = qk_fp8 ? 1 : esz, kesz = qk_fp8 ? 1 : esz;
+  const int64_t q_bytes = extent_bytes(B, H, Sq, D, q_stride, qesz);
+  const int64_t k_bytes = Skv > 0 ? extent_bytes(B, H, Skv, D, kv_stride, kesz) : 0;
+  const int64_t v_bytes = Skv > 0 ? extent_bytes(B, H, Skv, D, kv_stride, esz) : 0;
+  const int64_t out_bytes = mul3(P, rows, D * (state_dtype == AS_BF16 ? 2 : 4));
+  const int64_t lse_bytes = mul3(P, rows, 4);
+  if (q_bytes < 0 || k_bytes < 0 || v_bytes < 0 || out_bytes < 0 || lse_bytes < 0)
+    return fail(AS_ERR_UNSUPPORTED, "tensor extents overflow 64-bit byte counts");
+  if (overlap(out, (size_t)out_bytes, lse, (size_t)lse_bytes)) return fail(AS_ERR_INVALID_ARG, "out and lse overlap");
+  const void* ins[3] = {q, k, v};
+  const int64_t in_bytes[3] = {q_bytes, k_bytes, v_bytes};
+  for (int j = 0; j < 3; ++j)
+    if (overlap(out, (size_t)out_bytes, ins[j], (size_t)in_bytes[j]) ||
+        overlap(lse, (size_t)lse_bytes, ins[j], (size_t)in_bytes[j]))
+      return fail(AS_ERR_INVALID_ARG, "out or lse overlaps input %c", "qkv"[j]);
 
   as::AttnArgs a;
   memset(&a, 0, sizeof(a));
@@ -139,17 +189,24 @@ as_status merge_impl(int32_t n, const void* const* outs, const float* const* lse
   if (D < 4 || D > 1024 || D % 4) return fail(AS_ERR_INVALID_ARG, "D=%lld must be a multiple of 4 in [4, 1024]", (long long)D);
   if (!outs || !lses) return fail(AS_ERR_INVALID_ARG, "NULL pointer list");
   if (rows == 0) return ok();
+  if (rows > kMaxRows) return fail(AS_ERR_UNSUPPORTED, "rows=%lld too large", (long long)rows);
   if (!out || !lse) return fail(AS_ERR_INVALID_ARG, "NULL output pointer");
   // OUT is read and written 4 elements at a time: 16 bytes of fp32, 8 of bf16
   const size_t ain = in_dtype == AS_BF16 ? 8 : 16, aout = out_dtype == AS_BF16 ? 8 : 16;
   if (!aligned(out, aout) || !aligned(lse, 4))
     return fail(AS_ERR_INVALID_ARG, "out must be %zu-byte and lse 4-byte aligned", aout);
+  const size_t in_bytes = (size_t)(rows * D) * (in_dtype == AS_BF16 ? 2 : 4);
+  const size_t out_bytes = (size_t)(rows * D) * (out_dtype == AS_BF16 ? 2 : 4);
+  const size_t lse_bytes = (size_t)rows * 4;
+  if (overlap(out, out_bytes, lse, lse_bytes)) return fail(AS_ERR_INVALID_ARG, "out and lse overlap");
   as::MergeArgs a;
   memset(&a, 0, sizeof(a));
   for (int32_t i = 0; i < n; ++i) {
     if (!outs[i] || !lses[i]) return fail(AS_ERR_INVALID_ARG, "input %d has a NULL pointer", i);
     if (!aligned(outs[i], ain) || !aligned(lses[i], 4)) return fail(AS_ERR_INVALID_ARG, "input %d is misaligned", i);
-    if (outs[i] == out || lses[i] == lse) return fail(AS_ERR_INVALID_ARG, "input %d aliases the output", i);
+    if (overlap(outs[i], in_bytes, out, out_bytes) || overlap(outs[i], in_bytes, lse, lse_bytes) ||
+        overlap(lses[i], lse_bytes, out, out_bytes) || overlap(lses[i], lse_bytes, lse, lse_bytes))
+      return fail(AS_ERR_INVALID_ARG, "input %d overlaps the output", i);
     a.outs[i] = outs[i];
     a.lses[i] = lses[i];
   }
@@ -158,11 +215,6 @@ as_status merge_impl(int32_t n, const void* const* outs, const float* const* lse
   a.vec2 = D % 8 == 0 && aligned(out, 16);
   for (int32_t i = 0; i < n; ++i) a.vec2 = a.vec2 && aligned(outs[i], 16);
   return hip_status(as::launch_merge(a, stream), "merge launch");
-}
-
-bool overlap(const void* a, size_t na, const void* b, size_t nb) {
-  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
-  return x < y + nb && y < x + na;
 }
 
 }  // namespace
@@ -208,6 +260,7 @@ as_status as_compose_groups(const void* outs, const float* lses, as_dtype in_dty
   if (rows < 0) return fail(AS_ERR_INVALID_ARG, "rows=%lld is negative", (long long)rows);
   if (D < 4 || D > 1024 || D % 4) return fail(AS_ERR_INVALID_ARG, "D=%lld must be a multiple of 4 in [4, 1024]", (long long)D);
   if (rows == 0) return ok();
+  if (rows > kMaxRows) return fail(AS_ERR_UNSUPPORTED, "rows=%lld too large", (long long)rows);
   if (!outs || !lses || !out || !lse) return fail(AS_ERR_INVALID_ARG, "NULL pointer");
   if (!aligned(outs, 16) || !aligned(out, 16) || !aligned(lses, 4) || !aligned(lse, 4))
     return fail(AS_ERR_INVALID_ARG, "OUT blocks must be 16-byte and LSE blocks 4-byte aligned");
@@ -218,6 +271,8 @@ as_status as_compose_groups(const void* outs, const float* lses, as_dtype in_dty
       overlap(outs, (size_t)(P * rows * D) * ein, lse, (size_t)(G * rows) * 4) ||
       overlap(lses, (size_t)(P * rows) * 4, out, (size_t)(G * rows * D) * eout))
     return fail(AS_ERR_INVALID_ARG, "outputs overlap the input blocks");
+  if (overlap(out, (size_t)(G * rows * D) * eout, lse, (size_t)(G * rows) * 4))
+    return fail(AS_ERR_INVALID_ARG, "out and lse overlap");
   as::MergeArgs a;
   memset(&a, 0, sizeof(a));
   a.base_out = outs; a.base_lse = lses; a.out = out; a.lse = lse;
@@ -237,7 +292,8 @@ as_status as_merge(int32_t n, const float* const* outs, const float* const* lses
 }
 
 size_t as_partition_contribution_workspace_size(int32_t P, int64_t rows, int64_t rows_per_group) {
-  if (P < 1 || P > AS_MAX_PARTITIONS || rows < 0 || rows_per_group < 1 || rows % rows_per_group) return 0;
+  if (P < 1 || P > AS_MAX_PARTITIONS || rows < 0 || rows > kMaxRows || rows_per_group < 1 || rows % rows_per_group)
+    return 0;
   const int64_t G = rows / rows_per_group;
   const int64_t chunks = (rows_per_group + as::kContribChunk - 1) / as::kContribChunk;
   return (size_t)(G * chunks * P) * sizeof(float);
@@ -255,13 +311,20 @@ as_status as_partition_contribution(const float* lse, int32_t P, int64_t rows, i
   if (!lse) return fail(AS_ERR_INVALID_ARG, "lse is NULL");
   if (!aligned(lse, 4) || (weights && !aligned(weights, 4)) || (scores && !aligned(scores, 4)))
     return fail(AS_ERR_INVALID_ARG, "misaligned pointer");
-  if ((int64_t)P * rows > ((int64_t)1 << 40)) return fail(AS_ERR_UNSUPPORTED, "P*rows too large");
+  if (rows > kMaxRows || (int64_t)P * rows > kMaxRows) return fail(AS_ERR_UNSUPPORTED, "P*rows too large");
   const size_t need = as_partition_contribution_workspace_size(P, rows, rows_per_group);
   if (scores) {
     if (!workspace) return fail(AS_ERR_INVALID_ARG, "workspace is NULL but scores were requested");
     if (workspace_bytes < need)
       return fail(AS_ERR_INVALID_ARG, "workspace of %zu bytes is smaller than the %zu bytes needed", workspace_bytes, need);
     if (!aligned(workspace, 16)) return fail(AS_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  }
+  {
+    const size_t lb = (size_t)(P * rows) * 4, wb = weights ? lb : 0;
+    const size_t sb = scores ? (size_t)((rows / rows_per_group) * P) * 4 : 0, kb = scores ? need : 0;
+    if (overlap(weights, wb, lse, lb) || overlap(scores, sb, lse, lb) || overlap(workspace, kb, lse, lb) ||
+        overlap(weights, wb, scores, sb) || overlap(weights, wb, workspace, kb) || overlap(scores, sb, workspace, kb))
+      return fail(AS_ERR_INVALID_ARG, "weights, scores, workspace and lse must not overlap");
   }
   as::ContribArgs a;
   memset(&a, 0, sizeof(a));
@@ -292,6 +355,13 @@ as_status as_state_norms(const float* a, const float* b, int32_t P, int64_t n, f
   if (workspace_bytes < need)
     return fail(AS_ERR_INVALID_ARG, "workspace of %zu bytes is smaller than the %zu bytes needed", workspace_bytes, need);
   if (!aligned(workspace, 16)) return fail(AS_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  {
+    const size_t ib = (size_t)(P * n) * 4, nb = (size_t)P * 4;
+    const void* bb = n > 0 ? b : nullptr;
+    if (overlap(norms, nb, a, ib) || overlap(norms, nb, bb, ib) || overlap(workspace, need, a, ib) ||
+        overlap(workspace, need, bb, ib) || overlap(workspace, need, norms, nb))
+      return fail(AS_ERR_INVALID_ARG, "norms, workspace and the inputs must not overlap");
+  }
   as::NormArgs g;
   memset(&g, 0, sizeof(g));
   g.a = a; g.b = (n > 0) ? b : nullptr; g.norms = norms; g.partial = static_cast<double*>(workspace);
@@ -320,6 +390,20 @@ as_status as_planner_decide(const float* anchor_norms, const float* local_drift,
   const void* ptrs[] = {anchor_norms, local_drift, weights, eps, alpha, delta, ase, compute, anchor};
   for (const void* p : ptrs)
     if (!aligned(p, 4)) return fail(AS_ERR_INVALID_ARG, "misaligned pointer");
+  {
+    const int32_t ge = group > P ? P : group;
+    const size_t G = (size_t)((P + ge - 1) / ge);
+    const void* ip[] = {anchor_norms, local_drift, weights, eps};
+    const size_t ib[] = {(size_t)P * 4, 4, (size_t)P * 4, 4};
+    const void* op[] = {alpha, delta, ase, compute, anchor};
+    const size_t ob[] = {(size_t)P * 4, (size_t)P * 4, G * 4, G * 4, 4};
+    for (int o = 0; o < 5; ++o) {
+      for (int i = 0; i < 4; ++i)
+        if (overlap(op[o], ob[o], ip[i], ib[i])) return fail(AS_ERR_INVALID_ARG, "an output overlaps an input");
+      for (int o2 = o + 1; o2 < 5; ++o2)
+        if (overlap(op[o], ob[o], op[o2], ob[o2])) return fail(AS_ERR_INVALID_ARG, "outputs overlap each other");
+    }
+  }
   as::PlanArgs g;
   memset(&g, 0, sizeof(g));
   g.anchor_norms = anchor_norms; g.local_drift = local_drift; g.weights = weights; g.eps = eps;
@@ -338,6 +422,8 @@ as_status as_planner_epsilon(const float* corr_norms, const float* weights, int3
   if (!corr_norms || !weights || !eps) return fail(AS_ERR_INVALID_ARG, "corr_norms, weights and eps must not be NULL");
   if (!aligned(corr_norms, 4) || !aligned(weights, 4) || !aligned(eps, 4))
     return fail(AS_ERR_INVALID_ARG, "misaligned pointer");
+  if (overlap(eps, 4, corr_norms, (size_t)P * 4) || overlap(eps, 4, weights, (size_t)P * 4))
+    return fail(AS_ERR_INVALID_ARG, "eps overlaps an input");
   as::PlanArgs g;
   memset(&g, 0, sizeof(g));
   g.corr_norms = corr_norms; g.weights = weights; g.eps_out = eps;

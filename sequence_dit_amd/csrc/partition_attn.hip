@@ -318,6 +318,9 @@ struct Wave {
   template <bool MASK>
   __device__ __forceinline__ void softmax(int valid, float c2, int half) {
     if (MASK) {  // keys past the end of the partition
+      // The mask is applied to scaled scores and the rest of the tile then runs with
+      // a unit scale: masking raw scores to -inf would give -inf * 0 = NaN for a zero
+      // softmax scale (or a zero fp8 factor), where every valid key must weigh e^0.
       // key = kb * 32 + 8 (r / 4) + 4 half + r % 4 >= valid, with the lane part moved to
       // the right: every comparison is an immediate against one register (per-key
       // indices would be hoisted out of the tile loop and held in ~30 VGPRs)
@@ -326,7 +329,8 @@ struct Wave {
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s[kb][r] = -INFINITY;
+          s[kb][r] = (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) ? -INFINITY : s[kb][r] * c2;
+      c2 = 1.0f;
     }
     float x = s[0][0];
 #pragma unroll
@@ -493,7 +497,14 @@ void attn_bf16_kernel(const AttnArgs a) {
 
   W w;
   const int qrow = q0 + wave * kRowsPerWave + l32;
+  // fp8 scores are in units of the two dequantisation factors of this (b, h)
+  float c2 = QK8 ? a.scale_log2 * a.q_scale[bh] * a.k_scale[bh] : a.scale_log2;
   if constexpr (QK8) {
+    // A negative product of the factors is moved into Q: flipping the sign bit of every
+    // E4M3 code negates its value exactly, and the softmax then sees a scale >= 0 (its
+    // per-tile maximum of raw scores is the maximum of the scaled ones).
+    const unsigned qsign = c2 < 0.f ? 0x80808080u : 0u;
+    c2 = fabsf(c2);
     const unsigned char* qp = reinterpret_cast<const unsigned char*>(a.q) + b * a.q_sb + hh * a.q_sh +
                               (int64_t)min(qrow, a.Sq - 1) * a.q_ss + 32 * half;
 #pragma unroll
@@ -502,8 +513,8 @@ void attn_bf16_kernel(const AttnArgs a) {
       const u32x4 x1 = *reinterpret_cast<const u32x4*>(qp + 64 * ds + 16);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        w.qf.v[ds][e] = qrow < a.Sq ? (int)x0[e] : 0;
-        w.qf.v[ds][4 + e] = qrow < a.Sq ? (int)x1[e] : 0;
+        w.qf.v[ds][e] = qrow < a.Sq ? (int)(x0[e] ^ qsign) : 0;
+        w.qf.v[ds][4 + e] = qrow < a.Sq ? (int)(x1[e] ^ qsign) : 0;
       }
     }
   } else {
@@ -524,8 +535,6 @@ void attn_bf16_kernel(const AttnArgs a) {
   w.l = 0.f;
   w.k_rd = l32 * L::KP + (QK8 ? 32 : 16) * half;
   w.v_rd = L::V0 + l32 * L::VP + 16 * half;
-  // fp8 scores are in units of the two dequantisation factors of this (b, h)
-  const float c2 = QK8 ? a.scale_log2 * a.q_scale[bh] * a.k_scale[bh] : a.scale_log2;
   constexpr int KB = Tile<D>::KB;
   const int T = (n + KB - 1) / KB;
 

@@ -92,7 +92,7 @@ def test_partition_attn_empty_problem_is_ok_without_gpu():
     assert attn(ranges=[], P=0)[0] == N.AS_OK
 
 
-def merge_call(n=2, rows=8, D=128, outs=None, lses=None, out=FAKE, lse=FAKE):
+def merge_call(n=2, rows=8, D=128, outs=None, lses=None, out=FAKE, lse=FAKE + 0x200000):
     outs = outs if outs is not None else [FAKE + 0x1000 * (i + 1) for i in range(n)]
     lses = lses if lses is not None else [FAKE + 0x100000 + 0x1000 * i for i in range(n)]
     op = (ctypes.c_void_p * max(1, len(outs)))(*outs)
@@ -111,7 +111,8 @@ def merge_call(n=2, rows=8, D=128, outs=None, lses=None, out=FAKE, lse=FAKE):
     (dict(out=FAKE + 8), N.AS_ERR_INVALID_ARG, "aligned"),
     (dict(outs=[FAKE + 0x1000, 0]), N.AS_ERR_INVALID_ARG, "input 1"),
     (dict(outs=[FAKE + 0x1000, FAKE + 0x2004]), N.AS_ERR_INVALID_ARG, "misaligned"),
-    (dict(outs=[FAKE, FAKE + 0x2000]), N.AS_ERR_INVALID_ARG, "aliases"),
+    (dict(outs=[FAKE, FAKE + 0x2000]), N.AS_ERR_INVALID_ARG, "overlaps the output"),
+    (dict(lse=FAKE), N.AS_ERR_INVALID_ARG, "out and lse overlap"),
 ])
 def test_merge_rejects(kw, status, text):
     st, msg = merge_call(**kw)
@@ -265,7 +266,8 @@ def test_partition_attn_states_rejects_bad_state_dtype():
     assert st == N.AS_ERR_INVALID_ARG and "state_dtype" in N.lib().as_last_error().decode()
 
 
-def merge_states_call(n=2, in_dt=N.AS_BF16, out_dt=N.AS_F32, rows=10, D=128, out=FAKE, lse=FAKE, ptrs=None):
+def merge_states_call(n=2, in_dt=N.AS_BF16, out_dt=N.AS_F32, rows=10, D=128, out=FAKE, lse=FAKE + 0x200000,
+                      ptrs=None):
     ptrs = ptrs if ptrs is not None else [FAKE + 0x1000 * (i + 1) for i in range(max(n, 1))]
     optrs = (ctypes.c_void_p * len(ptrs))(*ptrs)
     lptrs = (ctypes.c_void_p * len(ptrs))(*ptrs)
@@ -282,7 +284,7 @@ def merge_states_call(n=2, in_dt=N.AS_BF16, out_dt=N.AS_F32, rows=10, D=128, out
     (dict(out=FAKE + 8), N.AS_ERR_INVALID_ARG, "16-byte"),
     (dict(ptrs=[FAKE + 4, FAKE + 0x2000]), N.AS_ERR_INVALID_ARG, "misaligned"),
     (dict(in_dt=N.AS_F32, ptrs=[FAKE + 8, FAKE + 0x2000]), N.AS_ERR_INVALID_ARG, "misaligned"),
-    (dict(ptrs=[FAKE, FAKE + 0x1000], out=FAKE), N.AS_ERR_INVALID_ARG, "aliases"),
+    (dict(ptrs=[FAKE, FAKE + 0x1000], out=FAKE), N.AS_ERR_INVALID_ARG, "overlaps the output"),
 ])
 def test_merge_states_rejects(kw, status, text):
     st, msg = merge_states_call(**kw)
@@ -352,3 +354,209 @@ def test_partition_attn_fp8_rejects(kw, status, text):
 
 def test_partition_attn_fp8_empty_problem_is_ok_without_gpu():
     assert attn_fp8(Sq=0, q=0, out=0, lse=0, qsc=0, ksc=0)[0] == N.AS_OK
+
+
+# --------------------------------------------------------------------------- #
+# Aliasing: every output is checked against every input (and the other outputs)
+# on byte ranges, partial overlaps included; overlapping calls fail before any HIP call.
+# --------------------------------------------------------------------------- #
+
+QA, KA, VA, OA, LA = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
+# extents with the attn() shapes (B1 H2 Sq16 Skv64 D128, bf16): q 8192 B, k and v 32768 B,
+# out 2 x 32 x 128 x 4 = 32768 B, lse 256 B
+
+
+@pytest.mark.parametrize("kw,text", [
+    (dict(out=QA + 0x1000), "overlaps input q"),            # starts inside q
+    (dict(out=QA - 0x4000), "overlaps input q"),            # covers q's start
+    (dict(lse=VA + 0x7ff0), "overlaps input v"),            # last 16 bytes of v
+    (dict(lse=KA), "overlaps input k"),
+    (dict(lse=OA + 0x7f00), "out and lse overlap"),
+    (dict(out=QA + 16000, qs=(8192, 4096, 256)), "overlaps input q"),   # inside a strided q's span
+])
+def test_partition_attn_rejects_overlapping_outputs(kw, text):
+    args = dict(q=QA, k=KA, v=VA, out=OA, lse=LA)
+    args.update(kw)
+    st, msg = attn(**args)
+    assert st == N.AS_ERR_INVALID_ARG, msg
+    assert text in msg
+
+
+def test_partition_attn_fp8_rejects_overlapping_outputs():
+    # fp8 q is 1 byte per element: B1 H2 Sq16 D128 with strides (4096, 2048, 128) spans 4096 bytes
+    st, msg = attn_fp8(q=QA, k=KA, v=VA, qsc=0x600000, ksc=0x700000, out=QA + 4080, lse=LA)
+    assert st == N.AS_ERR_INVALID_ARG and "overlaps input q" in msg, msg
+    st, msg = attn_fp8(q=QA, k=KA, v=VA, qsc=0x600000, ksc=0x700000, out=OA, lse=OA + 0x10)
+    assert st == N.AS_ERR_INVALID_ARG and "out and lse overlap" in msg, msg
+
+
+def test_partition_attn_rejects_short_range_with_huge_stride():
+    """A tile reads up to 128 key rows from a range's start (past a shorter range's end, where the
+    hardware range check returns zeros): their 32-bit byte offsets must not wrap."""
+    st, msg = attn(q=QA, k=KA, v=VA, out=OA, lse=LA, Skv=2, ranges=[(0, 1)], kvs=(1 << 25, 1 << 24, 1 << 24))
+    assert st == N.AS_ERR_UNSUPPORTED and "2^31" in msg, msg
+
+
+def test_partition_attn_rejects_sizes_whose_products_overflow():
+    st, msg = attn(B=1 << 40, H=1 << 40)
+    assert st == N.AS_ERR_UNSUPPORTED and "65535" in msg, msg
+
+
+@pytest.mark.parametrize("kw,text", [
+    (dict(out=FAKE + 0x1000 + 64 * 4), "input 0 overlaps the output"),      # 64 floats into input 0's OUT
+    (dict(out=FAKE + 0x100000 - 0x800), "input 0 overlaps the output"),     # out's tail covers input 0's LSE
+    (dict(lse=FAKE + 0x2000 + 0xff0), "input 1 overlaps the output"),       # lse inside input 1's OUT
+    (dict(lse=FAKE + 0x101000 + 4), "input 1 overlaps the output"),         # lse one float into input 1's LSE
+])
+def test_merge_rejects_partial_overlaps(kw, text):
+    # inputs: OUT at FAKE + 0x1000 (i + 1) (8 rows x 128 x 4 = 4 KiB each), LSE at FAKE + 0x100000 + 0x1000 i
+    st, msg = merge_call(**kw)
+    assert st == N.AS_ERR_INVALID_ARG, msg
+    assert text in msg
+
+
+def test_merge_states_rejects_partial_overlap():
+    # bf16 inputs of 10 rows x 128 x 2 = 2560 bytes at FAKE + 0x1000 (i + 1); LSE blocks alias the OUT pointers
+    st, msg = merge_states_call(out=FAKE + 0x2000 + 0x900)
+    assert st == N.AS_ERR_INVALID_ARG and "overlaps the output" in msg, msg
+
+
+@pytest.mark.parametrize("kw", [dict(w=FAKE + 0x100), dict(s=FAKE + 0x40), dict(ws=FAKE),
+                                dict(lse=0x200000, w=0x300000, s=0x400000, ws=0x400010)])
+def test_contribution_rejects_overlaps(kw):
+    args = dict(lse=FAKE, w=0x200000, s=0x300000, ws=0x400000)
+    args.update(kw)
+    st, msg = contrib_call(**args)
+    assert st == N.AS_ERR_INVALID_ARG and "must not overlap" in msg, msg
+
+
+@pytest.mark.parametrize("kw", [dict(out=FAKE + 0x100), dict(b=0x300000, out=0x300000 + 0x1000),
+                                dict(ws=FAKE + 0x1000), dict(ws=0x200000 - 0x10, out=0x200000 - 4)])
+def test_state_norms_rejects_overlaps(kw):
+    args = dict(a=FAKE, out=0x200000, ws=0x400000)
+    args.update(kw)
+    st, msg = norms_call(**args)
+    assert st == N.AS_ERR_INVALID_ARG and "overlap" in msg, msg
+
+
+def test_planner_rejects_overlaps():
+    base = dict(an=0x100000, dr=0x110000, w=0x120000, eps=0x130000, alpha=0x140000, delta=0x150000,
+                ase=0x160000, comp=0x170000, anch=0x180000)
+    for kw in (dict(alpha=0x100000 + 16), dict(comp=0x120000), dict(anch=0x160000 + 4), dict(delta=0x140000 + 8)):
+        args = dict(base)
+        args.update(kw)
+        st, msg = decide_call(**args)
+        assert st == N.AS_ERR_INVALID_ARG and "overlap" in msg, (kw, msg)
+    st, msg = epsilon_call(corr=0x100000, w=0x120000, eps=0x100000 + 8)
+    assert st == N.AS_ERR_INVALID_ARG and "overlaps" in msg, msg
+
+
+# --------------------------------------------------------------------------- #
+# The Python binding: every tensor whose pointer reaches the library goes through the
+# device check, and caller-supplied outputs of the wrong dtype, layout or size are
+# refused before any library call. The library is replaced by a recorder here.
+# --------------------------------------------------------------------------- #
+
+class _Recorder:
+    def __init__(self):
+        self.calls = []
+
+    def __getattr__(self, name):
+        if name.endswith("_workspace_size"):
+            return lambda *a: 64
+        if name == "as_last_error":
+            return lambda: b""
+
+        def call(*args):
+            self.calls.append((name, args))
+            return N.AS_OK
+        return call
+
+
+def _pointers(args):
+    ptrs = []
+    for a in args:
+        if isinstance(a, ctypes.Array) and a._type_ is ctypes.c_void_p:
+            ptrs.extend(int(x) for x in a if x)
+        elif isinstance(a, int) and a > 4096:
+            ptrs.append(a)
+    return ptrs
+
+
+@pytest.fixture
+def recorded(monkeypatch):
+    import torch
+    rec = _Recorder()
+    checked = set()
+
+    def require_gpu(*ts):
+        for t in ts:
+            if t is not None:
+                checked.add(t.data_ptr())
+
+    monkeypatch.setattr(N, "_lib", rec)
+    monkeypatch.setattr(N, "_require_gpu", require_gpu)
+    monkeypatch.setattr(N, "_stream", lambda t: 0)
+    return torch, rec, checked
+
+
+def test_binding_device_checks_cover_every_pointer(recorded):
+    torch, rec, checked = recorded
+    bf, f32 = torch.bfloat16, torch.float32
+    q = torch.zeros(1, 2, 8, 64, dtype=bf)
+    kv = torch.zeros(1, 2, 32, 64, dtype=bf)
+    out = torch.zeros(2, 1, 2, 8, 64)
+    lse = torch.zeros(2, 1, 2, 8)
+    N.partition_attn(q, kv, kv.clone(), [(0, 16), (16, 32)], out=out, lse=lse)
+    N.partition_attn_states(q, kv, kv.clone(), [(0, 16), (16, 32)], state_dtype=bf)
+    q8, k8 = q.to(torch.float8_e4m3fn), kv.to(torch.float8_e4m3fn)
+    N.partition_attn_fp8(q8, k8, kv, torch.ones(1, 2), torch.ones(1, 2), [(0, 32)])
+    states, lses = torch.zeros(3, 16, 64), torch.zeros(3, 16)
+    N.merge(list(states), list(lses))
+    N.merge_states(list(states.to(bf)), list(lses), f32)
+    N.compose_groups(states, lses, 2)
+    N.partition_contribution(lses, 8)
+    N.state_norms(states.view(3, -1), torch.ones(3, 16 * 64))
+    N.planner_decide(torch.ones(4), torch.ones(1), torch.ones(4), torch.ones(1), 1, 2, 0.5)
+    N.planner_epsilon(torch.ones(4), torch.ones(4), 1, 2, 0.5)
+    assert len(rec.calls) == 10, [c[0] for c in rec.calls]
+    for name, args in rec.calls:
+        missing = [p for p in _pointers(args) if p not in checked]
+        assert not missing, f"{name}: pointers {missing} skipped the device check"
+
+
+@pytest.mark.parametrize("case", ["attn_out_small", "attn_out_dtype", "attn_lse_noncontig", "merge_out_bf16",
+                                  "merge_lse_small", "merge_states_out_dtype", "compose_out_small",
+                                  "norms_small", "norms_workspace_small", "contrib_workspace_small",
+                                  "epsilon_eps_small"])
+def test_binding_refuses_bad_outputs_before_calling(recorded, case):
+    torch, rec, _ = recorded
+    bf = torch.bfloat16
+    q = torch.zeros(1, 2, 8, 64, dtype=bf)
+    kv = torch.zeros(1, 2, 32, 64, dtype=bf)
+    states, lses = torch.zeros(3, 16, 64), torch.zeros(3, 16)
+    calls = {
+        "attn_out_small": lambda: N.partition_attn(q, kv, kv, [(0, 32)], out=torch.zeros(1, 1, 2, 7, 64)),
+        "attn_out_dtype": lambda: N.partition_attn(q, kv, kv, [(0, 32)], out=torch.zeros(1, 1, 2, 8, 64, dtype=bf)),
+        "attn_lse_noncontig": lambda: N.partition_attn(q, kv, kv, [(0, 32)], lse=torch.zeros(1, 1, 8, 2).transpose(2, 3)),
+        "merge_out_bf16": lambda: N.merge(list(states), list(lses), out=torch.zeros(16, 64, dtype=bf)),
+        "merge_lse_small": lambda: N.merge(list(states), list(lses), lse=torch.zeros(15)),
+        "merge_states_out_dtype": lambda: N.merge_states(list(states), list(lses), torch.float32,
+                                                         out=torch.zeros(16, 64, dtype=bf)),
+        "compose_out_small": lambda: N.compose_groups(states, lses, 2, out=torch.zeros(1, 16, 64)),
+        "norms_small": lambda: N.state_norms(states.view(3, -1), norms=torch.zeros(2)),
+        "norms_workspace_small": lambda: N.state_norms(states.view(3, -1), workspace=torch.zeros(8, dtype=torch.uint8)),
+        "contrib_workspace_small": lambda: N.partition_contribution(lses, 8, workspace=torch.zeros(8, dtype=torch.uint8)),
+        "epsilon_eps_small": lambda: N.planner_epsilon(torch.ones(4), torch.ones(4), 1, 2, 0.5, eps=torch.zeros(0)),
+    }
+    with pytest.raises(ValueError):
+        calls[case]()
+    assert rec.calls == [], "the library was called"
+
+
+def test_binding_refuses_cpu_outputs():
+    """With the real device check, a CPU output is refused like a CPU input (before any library call)."""
+    import torch
+    x = torch.zeros(2, 16, 64)
+    with pytest.raises(ValueError, match="HIP device"):
+        N.merge(list(x), list(torch.zeros(2, 16)))

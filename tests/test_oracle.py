@@ -229,6 +229,17 @@ def check_reuse(orc):
     assert errs[0] < 1e-25 < errs[1] < errs[2]
 
 
+def check_mse(orc):
+    """The reported error measure: hand-worked value (golden file), a 3-d layout of the same
+    numbers, and the zero of identical inputs."""
+    g = load_golden()
+    a, b = np.array(g["mse_a"]), np.array(g["mse_b"])
+    assert orc.mse(a, b) == g["mse"][0][0]
+    assert orc.mse(a.reshape(2, 1, 2), b.reshape(2, 1, 2)) == g["mse"][0][0]
+    assert orc.mse(b, a) == g["mse"][0][0]
+    assert orc.mse(a, a) == 0.0
+
+
 def check_compose_groups(orc):
     g = np.random.default_rng(21)
     P, rows, D = 7, 5, 3
@@ -410,7 +421,7 @@ FP8_ALL = _fp8_table()
 
 PINS = [check_golden, check_bruteforce_loops, check_states_vs_sdpa, check_merge_equals_full,
         check_identity_bitexact, check_closed_forms, check_contribution, check_reuse,
-        check_compose_groups, check_planner_golden, check_norms, check_planner_invariants, check_epsilon, check_fp8]
+        check_compose_groups, check_mse, check_planner_golden, check_norms, check_planner_invariants, check_epsilon, check_fp8]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -488,6 +499,10 @@ MUTANTS = {
     "score sums instead of means": (".mean(axis=2).T", ".sum(axis=2).T"),
     "reuse caches the new step": ("c_out, c_lse = merge(out_t[far], lse_t[far])",
                                   "c_out, c_lse = merge(_f64(out_t1)[far], _f64(lse_t1)[far])"),
+    "mse as a root": ("return float(np.mean((_f64(a) - _f64(b)) ** 2))",
+                      "return float(np.sqrt(np.mean((_f64(a) - _f64(b)) ** 2)))"),
+    "mse of absolute differences": ("np.mean((_f64(a) - _f64(b)) ** 2)", "np.mean(np.abs(_f64(a) - _f64(b)))"),
+    "mse summed": ("np.mean((_f64(a) - _f64(b)) ** 2)", "np.sum((_f64(a) - _f64(b)) ** 2)"),
     "range end off by one": ("k[b, h, s:e], v[b, h, s:e]", "k[b, h, s:e + 1], v[b, h, s:e + 1]"),
     "group overlaps the next one": ("merge(outs[k:k + group], lses[k:k + group])",
                                     "merge(outs[k:k + group + 1], lses[k:k + group + 1])"),
