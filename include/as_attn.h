@@ -224,6 +224,29 @@ as_status as_partition_contribution(const float* lse, int32_t P, int64_t rows, i
                                     size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * as_partition_contribution_noalloc - as_partition_contribution for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. It takes no workspace; the per-chunk partial sums of the score
+ * reduction live in a static device buffer of AS_CONTRIBUTION_SCRATCH_BYTES that the
+ * library holds on every device it runs on until the process ends. Neither this call
+ * nor its first-call setup allocates or frees memory.
+ *
+ * Sizes: with scores requested, as_partition_contribution_workspace_size(P, rows,
+ * rows_per_group) must not exceed AS_CONTRIBUTION_SCRATCH_BYTES, else AS_ERR_INVALID_ARG
+ * (the long-video anchor, 32 partitions x 24 groups of 3840 rows, needs 46080 bytes).
+ * Sharing: every call on one device uses that device's single buffer, and it keeps the
+ * last call's contents (nothing in it needs to start at zero: each call overwrites what
+ * it reads). Calls whose work overlaps in time on one device (different streams, or
+ * threads without ordering between them) race on it; issue them on one stream or order
+ * them. The stream must belong to the current device; the first call on a device
+ * looks up the buffer's address there. Every other argument and rule is as for
+ * as_partition_contribution.
+ */
+#define AS_CONTRIBUTION_SCRATCH_BYTES ((size_t)1 << 20)
+as_status as_partition_contribution_noalloc(const float* lse, int32_t P, int64_t rows, int64_t rows_per_group,
+                                            float* weights, float* scores, hipStream_t stream);
+
+/*
  * Anchor-guided planner statistics.
  *   Source: DiTango review page (pith.science): "What carries the argument" (the
  *   group error ASE(G_i, t) = sum over the group of w(j, t) * delta(j, t, t_c), Eq. 12),

@@ -24,7 +24,8 @@ AS_MAX_MERGE = 64
 EXPORTS = ("as_partition_attn", "as_merge", "as_partition_attn_states", "as_partition_attn_fp8",
            "as_merge_states", "as_compose_groups",
            "as_partition_contribution_workspace_size",
-           "as_partition_contribution", "as_state_norms_workspace_size", "as_state_norms",
+           "as_partition_contribution", "as_partition_contribution_noalloc",
+           "as_state_norms_workspace_size", "as_state_norms",
            "as_planner_decide", "as_planner_epsilon", "as_status_string", "as_last_error")
 
 _lib = None
@@ -85,6 +86,10 @@ def lib() -> ctypes.CDLL:
         L.as_partition_contribution.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                                 ctypes.c_void_p]
+        L.as_partition_contribution_noalloc.restype = ctypes.c_int
+        L.as_partition_contribution_noalloc.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                                        ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                                        ctypes.c_void_p]
         L.as_state_norms_workspace_size.restype = ctypes.c_size_t
         L.as_state_norms_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int64]
         L.as_state_norms.restype = ctypes.c_int
@@ -377,6 +382,30 @@ def partition_contribution(lse: torch.Tensor, rows_per_group: int, want_weights:
                                           workspace.data_ptr() if workspace is not None else None,
                                           ws_bytes, _stream(lse)))
     return w, s
+
+
+CONTRIBUTION_SCRATCH_BYTES = 1 << 20   # AS_CONTRIBUTION_SCRATCH_BYTES
+
+
+def partition_contribution_noalloc(lse: torch.Tensor, rows_per_group: int, weights: Optional[torch.Tensor] = None,
+                                   scores: Optional[torch.Tensor] = None):
+    """as_partition_contribution_noalloc: weights [P, rows] and/or scores [rows/rows_per_group, P] written
+    into caller tensors (either may be None), with no workspace and no allocation in the library."""
+    if lse.dim() < 1:
+        raise ValueError("lse must be [P, ...]")
+    P = lse.shape[0]
+    rows = lse.numel() // max(P, 1)
+    _check_buf(lse, "lse", torch.float32, P * rows)
+    if weights is not None:
+        _check_buf(weights, "weights", torch.float32, P * rows)
+    if scores is not None:
+        if rows_per_group < 1 or rows % rows_per_group:
+            raise ValueError("rows_per_group must divide the number of rows")
+        _check_buf(scores, "scores", torch.float32, (rows // rows_per_group) * P)
+    _require_gpu(lse, weights, scores)
+    check(lib().as_partition_contribution_noalloc(lse.data_ptr(), P, rows, rows_per_group, _ptr(weights),
+                                                  _ptr(scores), _stream(lse)))
+    return weights, scores
 
 
 # --------------------------------------------------------------------------- #

@@ -299,9 +299,12 @@ size_t as_partition_contribution_workspace_size(int32_t P, int64_t rows, int64_t
   return (size_t)(G * chunks * P) * sizeof(float);
 }
 
-as_status as_partition_contribution(const float* lse, int32_t P, int64_t rows, int64_t rows_per_group,
-                                    float* weights, float* scores, void* workspace,
-                                    size_t workspace_bytes, hipStream_t stream) {
+namespace {
+// Shared by as_partition_contribution (caller workspace) and
+// as_partition_contribution_noalloc (library scratch, noalloc = true).
+as_status contribution_impl(const float* lse, int32_t P, int64_t rows, int64_t rows_per_group, float* weights,
+                            float* scores, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                            bool noalloc) {
   if (P < 1 || P > AS_MAX_PARTITIONS) return fail(AS_ERR_INVALID_ARG, "P=%d outside [1, %d]", P, AS_MAX_PARTITIONS);
   if (rows < 0) return fail(AS_ERR_INVALID_ARG, "rows=%lld is negative", (long long)rows);
   if (rows_per_group < 1) return fail(AS_ERR_INVALID_ARG, "rows_per_group=%lld must be >= 1", (long long)rows_per_group);
@@ -313,7 +316,10 @@ as_status as_partition_contribution(const float* lse, int32_t P, int64_t rows, i
     return fail(AS_ERR_INVALID_ARG, "misaligned pointer");
   if (rows > kMaxRows || (int64_t)P * rows > kMaxRows) return fail(AS_ERR_UNSUPPORTED, "P*rows too large");
   const size_t need = as_partition_contribution_workspace_size(P, rows, rows_per_group);
-  if (scores) {
+  if (noalloc && scores && need > as::kContribScratchBytes)
+    return fail(AS_ERR_INVALID_ARG, "scores of these sizes need %zu bytes of scratch; the library holds %zu",
+                need, as::kContribScratchBytes);
+  if (scores && !noalloc) {
     if (!workspace) return fail(AS_ERR_INVALID_ARG, "workspace is NULL but scores were requested");
     if (workspace_bytes < need)
       return fail(AS_ERR_INVALID_ARG, "workspace of %zu bytes is smaller than the %zu bytes needed", workspace_bytes, need);
@@ -321,18 +327,37 @@ as_status as_partition_contribution(const float* lse, int32_t P, int64_t rows, i
   }
   {
     const size_t lb = (size_t)(P * rows) * 4, wb = weights ? lb : 0;
-    const size_t sb = scores ? (size_t)((rows / rows_per_group) * P) * 4 : 0, kb = scores ? need : 0;
+    const size_t sb = scores ? (size_t)((rows / rows_per_group) * P) * 4 : 0, kb = scores && !noalloc ? need : 0;
     if (overlap(weights, wb, lse, lb) || overlap(scores, sb, lse, lb) || overlap(workspace, kb, lse, lb) ||
         overlap(weights, wb, scores, sb) || overlap(weights, wb, workspace, kb) || overlap(scores, sb, workspace, kb))
       return fail(AS_ERR_INVALID_ARG, "weights, scores, workspace and lse must not overlap");
   }
+  float* partial = nullptr;
+  if (scores && noalloc) {
+    const hipError_t e = as::contribution_scratch(&partial);
+    if (e != hipSuccess) return hip_status(e, "scratch address lookup");
+  } else if (scores) {
+    partial = static_cast<float*>(workspace);
+  }
   as::ContribArgs a;
   memset(&a, 0, sizeof(a));
   a.lse = lse; a.weights = weights; a.scores = scores;
-  a.partial = scores ? static_cast<float*>(workspace) : nullptr;
+  a.partial = partial;
   a.rows = rows; a.rows_per_group = rows_per_group; a.P = P;
   a.chunks_per_group = (int32_t)((rows_per_group + as::kContribChunk - 1) / as::kContribChunk);
   return hip_status(as::launch_contribution(a, stream), "partition_contribution launch");
+}
+}  // namespace
+
+as_status as_partition_contribution(const float* lse, int32_t P, int64_t rows, int64_t rows_per_group,
+                                    float* weights, float* scores, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+  return contribution_impl(lse, P, rows, rows_per_group, weights, scores, workspace, workspace_bytes, stream, false);
+}
+
+as_status as_partition_contribution_noalloc(const float* lse, int32_t P, int64_t rows, int64_t rows_per_group,
+                                            float* weights, float* scores, hipStream_t stream) {
+  return contribution_impl(lse, P, rows, rows_per_group, weights, scores, nullptr, 0, stream, true);
 }
 
 

@@ -118,4 +118,9 @@ hipError_t launch_planner_epsilon(const PlanArgs& a, hipStream_t stream);
 constexpr int kContribChunk = 256;
 hipError_t launch_contribution(const ContribArgs& a, hipStream_t stream);
 
+// Library-owned scratch of the allocation-free contribution entry point: its size,
+// and its device address on the current device (looked up once per device).
+constexpr size_t kContribScratchBytes = AS_CONTRIBUTION_SCRATCH_BYTES;
+hipError_t contribution_scratch(float** ptr);
+
 }  // namespace as

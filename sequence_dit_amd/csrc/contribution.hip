@@ -10,15 +10,45 @@
 // the LSE values (forming L* = M + ln S first would round L* to the ulp of M).
 // w is optionally written; for scores, the w of 32 partitions x 256 rows go
 // through LDS and are summed in a fixed order (32-row runs, then the 8 runs) into
-// one partial per (group, chunk, i) in the caller's workspace.
+// one partial per (group, chunk, i) in the caller's workspace (for the
+// allocation-free entry point, in the library's static scratch instead).
 // Launch 2: one wave per (group, i) adds the chunk partials (lane-strided, then a
 // butterfly). No atomics, so scores are bitwise reproducible.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <mutex>
+
 #include "as_internal.h"
 
+// Partial sums of the allocation-free entry point (as_partition_contribution_noalloc):
+// one copy per device, held until the process ends. Host code must not pass this
+// name to a kernel (on the host it is only a stand-in for the device variable): the
+// device address comes from contribution_scratch().
+static __device__ __align__(256) float scratch[as::kContribScratchBytes / sizeof(float)];
+
 namespace as {
+
+hipError_t contribution_scratch(float** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static float* per_device[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!per_device[dev]) {
+    // once per device, with that device current: its own copy of the array
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    per_device[dev] = static_cast<float*>(p);
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
+}
+
 namespace {
 
 constexpr int kThreads = kContribChunk;  // one row per thread

@@ -560,3 +560,18 @@ def test_binding_refuses_cpu_outputs():
     x = torch.zeros(2, 16, 64)
     with pytest.raises(ValueError, match="HIP device"):
         N.merge(list(x), list(torch.zeros(2, 16)))
+
+
+def test_contribution_noalloc_rejects_sizes_beyond_its_scratch():
+    """The allocation-free entry point holds AS_CONTRIBUTION_SCRATCH_BYTES of partial sums per device:
+    larger score reductions are refused on the host, before any HIP call."""
+    L = N.lib()
+    P, rpg = 256, 256
+    rows = rpg * 1025          # 1025 groups x 1 chunk x 256 partitions x 4 bytes > 1 MiB
+    assert L.as_partition_contribution_workspace_size(P, rows, rpg) > N.CONTRIBUTION_SCRATCH_BYTES
+    st = L.as_partition_contribution_noalloc(FAKE, P, rows, rpg, 0, 0x200000000, None)
+    assert st == N.AS_ERR_INVALID_ARG and "scratch" in L.as_last_error().decode()
+    st = L.as_partition_contribution_noalloc(FAKE, 0, rows, rpg, 0, FAKE, None)
+    assert st == N.AS_ERR_INVALID_ARG
+    # weights only need no scratch at all; nothing requested enqueues nothing
+    assert L.as_partition_contribution_noalloc(FAKE, P, rows, rpg, 0, 0, None) == N.AS_OK
