@@ -31,16 +31,20 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5000.0
 PEAK_MIXED_TFLOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "partition_attn_traffic.txt")
-ATTN_SOURCE = os.path.join(ROOT, "sequence_dit_amd", "csrc", "partition_attn.hip")
+ATTN_SOURCES = [os.path.join(ROOT, "sequence_dit_amd", "csrc", f) for f in ("attn_kernel.h", "partition_attn.hip")]
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def source_digest(path=ATTN_SOURCE):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def source_digest(paths=ATTN_SOURCES):
+    """sha256 over the attention kernel's sources (the template and its bf16 launcher)."""
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic():
@@ -157,6 +161,86 @@ def shape_sweep(N, inputs, torch, dev, reps=10):
                                           "frac_roofline": round(t_floor / t, 4)}
         del q, k, v, out, lse
     del scratch
+    return res
+
+
+def merge_sweep(N, torch, dev, state_out, state_lse, far, near_plus_cached, reps=10):
+    """as_merge alone, warm (back-to-back) and cold (a 512 MB scratch write before each launch, outside
+    its events, so the 256 MB MALL holds none of the inputs): the 32-way composition of all partition
+    states (the long-video workload's P-way merge), the 28-way composition of the far ones, and the
+    5-way merge of a reuse step. Median launch time; bytes = (k + 1) * rows * (4D + 4)."""
+    res = {}
+    scratch = torch.empty(512 << 18, dtype=torch.float32, device=dev)
+    rows = state_lse[0].numel()
+    D = state_out.shape[-1]
+    out = torch.empty(state_out.shape[1:], dtype=torch.float32, device=dev)
+    lse = torch.empty(state_lse.shape[1:], dtype=torch.float32, device=dev)
+    cases = (("merge_all_32", list(range(state_out.shape[0])), state_out, state_lse),
+             ("merge_cached_28", far, state_out, state_lse),
+             ("merge_step_5", list(range(near_plus_cached[0].shape[0])), near_plus_cached[0], near_plus_cached[1]))
+    for name, idx, so, sl in cases:
+        outs, lses = [so[i] for i in idx], [sl[i] for i in idx]
+        by = (len(idx) + 1) * rows * (4 * D + 4)
+        for mode in ("warm", "cold"):
+            for _ in range(2):
+                N.merge(outs, lses, out=out, lse=lse)
+            ev = []
+            for _ in range(reps):
+                if mode == "cold":
+                    scratch.fill_(1.0)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                N.merge(outs, lses, out=out, lse=lse)
+                b.record()
+                ev.append((a, b))
+            torch.cuda.synchronize()
+            ms = sorted(a.elapsed_time(b) for a, b in ev)
+            t = ms[len(ms) // 2]
+            res[f"{name}_{mode}"] = {"k": len(idx), "ms": round(t, 4), "GB/s": round(by / t / 1e6, 1),
+                                     "frac_hbm": round(by / t / 1e6 / PEAK_HBM_GBPS, 4)}
+    del scratch, out, lse
+    return res
+
+
+def grouped_sweep(runner, N, torch, q, k, v, q1, k1, v1, steps, ms_step, step_flops, attn_flops):
+    """The reuse step on grouped launches: the anchor composes the far partitions in groups of 4 inside
+    the attention epilogue (then a 7-way merge instead of the 28-way one), the next step folds the
+    cached state into the near partitions' composed state in one launch (near_group None) or in two
+    groups plus a 3-way merge (near_group 2). Whole step timed like the main one, and per call."""
+    res = {}
+    for ng in (None, 2):
+        tag = "" if ng is None else f"_near{ng}"
+        runner.timer = None
+        runner.anchor_grouped(q, k, v, 4)
+        runner.step_grouped(q1, k1, v1, ng)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            runner.anchor_grouped(q, k, v, 4)
+            runner.step_grouped(q1, k1, v1, ng)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / steps
+        res[f"step_grouped{tag}"] = {"ms": round(t, 4), "TFLOP/s": round(step_flops / t / 1e9, 1),
+                                     "speedup_vs_ungrouped": round(ms_step / t, 3)}
+        runner.timer = []
+        for _ in range(max(1, steps // 2)):
+            runner.anchor_grouped(q, k, v, 4)
+            runner.step_grouped(q1, k1, v1, ng)
+        torch.cuda.synchronize()
+        times = {}
+        for name, a, b in runner.timer:
+            times.setdefault(name, []).append(a.elapsed_time(b))
+        for name, ts in times.items():
+            ms = sum(ts) / len(ts)
+            entry = {"ms": round(ms, 4)}
+            base = {"attn_anchor_grouped": "attn_anchor", "attn_fresh_grouped": "attn_fresh"}.get(name)
+            if base:
+                entry["TFLOP/s"] = round(attn_flops[base] / ms / 1e9, 1)
+                entry["frac_mfma"] = round(attn_flops[base] / ms / 1e9 / PEAK_BF16_TFLOPS, 4)
+            res[f"{name}{tag}"] = entry
+    runner.timer = None
     return res
 
 
@@ -433,6 +517,16 @@ def main():
                 "avg_launch_ms": round(attn_ms / attn_launches, 4)}
 
     if reuse:
+        log("grouped launches (composition in the attention epilogue)")
+        kernels.update(grouped_sweep(runner, N, torch, q, k, v, q1, k1, v1, args.steps, ms_step, step_flops,
+                                     attn_flops))
+        log("merges warm and cold (32-way, 28-way, 5-way)")
+        runner.timer = None
+        runner.anchor(q, k, v)
+        runner.step(q1, k1, v1)
+        torch.cuda.synchronize()
+        kernels.update(merge_sweep(N, torch, dev, runner.state_out, runner.state_lse, runner.far,
+                                   (runner.step_out, runner.step_lse)))
         log("image and video DiT shapes, warm and cold")
         kernels.update(shape_sweep(N, inputs, torch, dev))
 

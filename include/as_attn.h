@@ -49,8 +49,10 @@ typedef enum {
 } as_status;
 
 typedef enum {
-  AS_BF16 = 0, /* bfloat16 Q/K/V: QK^T and PV on bf16 MFMA, fp32 accumulation and softmax */
-  AS_F32 = 1   /* float32 Q/K/V: fp32 arithmetic throughout (accuracy path) */
+  AS_BF16 = 0,     /* bfloat16 Q/K/V: QK^T and PV on bf16 MFMA, fp32 accumulation and softmax */
+  AS_F32 = 1,      /* float32 Q/K/V: fp32 arithmetic throughout (accuracy path) */
+  AS_FP8_E4M3 = 2  /* as_partition_attn_grouped only: fp8 E4M3 Q/K codes with per-(b, h)
+                      factors, bfloat16 V (as for as_partition_attn_fp8) */
 } as_dtype;
 
 #define AS_MAX_PARTITIONS 256 /* partitions per as_partition_attn call */
@@ -165,6 +167,43 @@ as_status as_partition_attn_fp8(const void* q, const void* k, const void* v, con
                                 const int64_t q_stride[3], const int64_t kv_stride[3],
                                 const int32_t* kv_ranges, int32_t P, float scale, as_dtype state_dtype,
                                 void* out, float* lse, hipStream_t stream);
+
+/*
+ * as_partition_attn_grouped - partition attention whose epilogue composes the states of
+ * consecutive partitions. For every group g of the range list (partitions
+ * group_starts[g] .. group_starts[g + 1] - 1) it writes the composed state of the group's
+ * partitions, i.e. as_merge of their as_partition_attn states, from one pass over their
+ * keys without writing any per-partition OUT; optionally the LSE of every partition; and
+ * optionally composes a given state (such as the cached composed state of other
+ * partitions) into group 0's result.
+ *   Source: DiTango review page (pith.science), referee report summary ("ring-based
+ *   attention composition" and "memory-aware state merging"); axiom ledger (Eq. 1-2:
+ *   associative, commutative composition); "If this is right" (composed states merged
+ *   into coarser groups).
+ *
+ * dtype         AS_BF16 (q, k, v bfloat16) or AS_FP8_E4M3 (q, k E4M3 codes with q_scale,
+ *               k_scale and strides as for as_partition_attn_fp8; v bfloat16). D is 64
+ *               or 128.
+ * q_scale, k_scale  as for as_partition_attn_fp8 (AS_FP8_E4M3 only; ignored for AS_BF16).
+ * kv_ranges, P  as for as_partition_attn, with 1 <= P <= AS_MAX_PARTITIONS.
+ * group_starts  HOST int32 [G + 1] with 0 = group_starts[0] <= ... <= group_starts[G] = P;
+ *               1 <= G <= AS_MAX_PARTITIONS; an empty group gives (0, -inf). Groups are
+ *               scheduled in list order: listing long groups first starts them first.
+ * fold_out, fold_lse  DEVICE float32 [B][H][Sq][D] (16-byte aligned) and [B][H][Sq], or
+ *               both NULL: a state composed into group 0's result as as_merge would.
+ * out, lse      DEVICE float32 [G][B][H][Sq][D] (16-byte aligned) and [G][B][H][Sq].
+ * part_lse      DEVICE float32 [P][B][H][Sq] or NULL: the LSE of every partition, equal to
+ *               as_partition_attn's lse (e.g. for as_partition_contribution).
+ * Outputs must not overlap each other or any input (checked). All other arguments and
+ * rules are as for as_partition_attn.
+ */
+as_status as_partition_attn_grouped(const void* q, const void* k, const void* v, as_dtype dtype,
+                                    const float* q_scale, const float* k_scale, int64_t B, int64_t H,
+                                    int64_t Sq, int64_t Skv, int64_t D, const int64_t q_stride[3],
+                                    const int64_t kv_stride[3], const int32_t* kv_ranges, int32_t P,
+                                    const int32_t* group_starts, int32_t G, float scale, const float* fold_out,
+                                    const float* fold_lse, float* out, float* lse, float* part_lse,
+                                    hipStream_t stream);
 
 /*
  * as_merge_states - as_merge for states whose OUT is stored as in_dtype, writing an

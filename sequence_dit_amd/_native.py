@@ -17,11 +17,12 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libas_attn.so")
 
 AS_OK, AS_ERR_INVALID_ARG, AS_ERR_UNSUPPORTED, AS_ERR_HIP = 0, 1, 2, 3
-AS_BF16, AS_F32 = 0, 1
+AS_BF16, AS_F32, AS_FP8_E4M3 = 0, 1, 2
 AS_MAX_PARTITIONS = 256
 AS_MAX_MERGE = 64
 
 EXPORTS = ("as_partition_attn", "as_merge", "as_partition_attn_states", "as_partition_attn_fp8",
+           "as_partition_attn_grouped",
            "as_merge_states", "as_compose_groups",
            "as_partition_contribution_workspace_size",
            "as_partition_contribution", "as_partition_contribution_noalloc",
@@ -73,6 +74,13 @@ def lib() -> ctypes.CDLL:
                                             ctypes.c_int64, ctypes.c_int64, c_i64p, c_i64p, c_i32p, ctypes.c_int32,
                                             ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_void_p]
+        L.as_partition_attn_grouped.restype = ctypes.c_int
+        L.as_partition_attn_grouped.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                                ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, c_i64p, c_i64p, c_i32p,
+                                                ctypes.c_int32, c_i32p, ctypes.c_int32, ctypes.c_float,
+                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                ctypes.c_void_p, ctypes.c_void_p]
         L.as_merge_states.restype = ctypes.c_int
         L.as_merge_states.argtypes = [ctypes.c_int32, c_vpp, c_vpp, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
                                       ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
@@ -152,6 +160,10 @@ def _check_workspace(t: torch.Tensor, need: int) -> int:
     if nbytes < need:
         raise ValueError(f"workspace of {nbytes} bytes is smaller than the {need} bytes needed")
     return nbytes
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return t.data_ptr() if t is not None else None
 
 
 def _i64(vals) -> ctypes.Array:
@@ -263,6 +275,68 @@ def _attn(q, k, v, kv_ranges, scale, out, lse, state_dtype):
     else:
         check(lib().as_partition_attn_states(*args, code, out.data_ptr(), lse.data_ptr(), _stream(q)))
     return out, lse
+
+
+def partition_attn_grouped(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_ranges: Sequence[Tuple[int, int]],
+                           group_starts: Sequence[int], scale: Optional[float] = None,
+                           fold: Optional[Tuple[torch.Tensor, torch.Tensor]] = None, want_part_lse: bool = True,
+                           q_scale: Optional[torch.Tensor] = None, k_scale: Optional[torch.Tensor] = None,
+                           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                           part_lse: Optional[torch.Tensor] = None):
+    """as_partition_attn_grouped: the composed state of every group of consecutive partitions
+    (group g = partitions group_starts[g] .. group_starts[g+1]-1), OUT [G,B,H,Sq,D] and LSE [G,B,H,Sq]
+    float32, and (want_part_lse) every partition's LSE [P,B,H,Sq]. q, k, v bfloat16, or q, k
+    float8_e4m3fn codes with float32 factors q_scale, k_scale [B,H] and v bfloat16. fold = (OUT
+    [B,H,Sq,D], LSE [B,H,Sq]) float32 state composed into group 0's result. Returns (out, lse, part_lse)."""
+    fp8 = q.dtype == torch.float8_e4m3fn
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or k.stride() != v.stride():
+        raise ValueError("q must be [B,H,Sq,D]; k and v [B,H,Skv,D] with equal strides")
+    if fp8:
+        if k.dtype != torch.float8_e4m3fn or v.dtype != torch.bfloat16:
+            raise ValueError("fp8 q needs fp8 k and bfloat16 v")
+        if q_scale is None or k_scale is None:
+            raise ValueError("fp8 q and k need their factors q_scale, k_scale")
+    elif q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise ValueError("q, k, v must be bfloat16 (or q, k float8_e4m3fn with bfloat16 v)")
+    B, H, Sq, D = q.shape
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != D:
+        raise ValueError("q and k/v disagree on B, H or D")
+    if q.stride(3) != 1 or k.stride(3) != 1:
+        raise ValueError("the head dimension must be contiguous")
+    if fp8:
+        for t in (q_scale, k_scale):
+            _check_buf(t, "q_scale/k_scale", torch.float32, B * H)
+    P, G = len(kv_ranges), len(group_starts) - 1
+    if G < 1:
+        raise ValueError("group_starts needs at least two entries")
+    if out is None:
+        out = torch.empty((G, B, H, Sq, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((G, B, H, Sq), dtype=torch.float32, device=q.device)
+    _check_buf(out, "out", torch.float32, G * B * H * Sq * D)
+    _check_buf(lse, "lse", torch.float32, G * B * H * Sq)
+    if want_part_lse:
+        if part_lse is None:
+            part_lse = torch.empty((P, B, H, Sq), dtype=torch.float32, device=q.device)
+        _check_buf(part_lse, "part_lse", torch.float32, P * B * H * Sq)
+    else:
+        part_lse = None
+    fo = fl = None
+    if fold is not None:
+        fo, fl = fold
+        _check_buf(fo, "fold OUT", torch.float32, B * H * Sq * D)
+        _check_buf(fl, "fold LSE", torch.float32, B * H * Sq)
+    _require_gpu(q, k, v, q_scale if fp8 else None, k_scale if fp8 else None, fo, fl, out, lse, part_lse)
+    flat = [int(x) for r in kv_ranges for x in r]
+    ranges = (ctypes.c_int32 * max(1, len(flat)))(*flat)
+    starts = (ctypes.c_int32 * len(group_starts))(*[int(x) for x in group_starts])
+    sc = float(D ** -0.5 if scale is None else scale)
+    check(lib().as_partition_attn_grouped(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), AS_FP8_E4M3 if fp8 else AS_BF16,
+        _ptr(q_scale) if fp8 else None, _ptr(k_scale) if fp8 else None, B, H, Sq, k.shape[2], D,
+        _i64(q.stride()[:3]), _i64(k.stride()[:3]), ranges, P, starts, G, sc, _ptr(fo), _ptr(fl),
+        out.data_ptr(), lse.data_ptr(), _ptr(part_lse), _stream(q)))
+    return out, lse, part_lse
 
 
 # --------------------------------------------------------------------------- #
@@ -414,10 +488,6 @@ def partition_contribution_noalloc(lse: torch.Tensor, rows_per_group: int, weigh
 
 def state_norms_workspace_size(P: int, n: int) -> int:
     return int(lib().as_state_norms_workspace_size(P, n))
-
-
-def _ptr(t: Optional[torch.Tensor]):
-    return t.data_ptr() if t is not None else None
 
 
 def state_norms(a: torch.Tensor, b: Optional[torch.Tensor] = None, norms: Optional[torch.Tensor] = None,

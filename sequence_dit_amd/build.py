@@ -21,12 +21,15 @@ LIB_NAME = "libas_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "partition_attn.hip", "merge.hip", "contribution.hip", "planner.hip"]
+SOURCES = ["api.hip", "partition_attn.hip", "partition_attn_fp8.hip", "partition_attn_grouped.hip", "merge.hip",
+           "contribution.hip", "planner.hip"]
 
 # Per-source flags. The attention kernels never see NaN (finite inputs, -inf only
 # as a max/exp operand), so NaN-honouring max and IEEE-mode operand
 # canonicalisation are switched off there: fmaxf becomes a single v_max/v_max3.
-SOURCE_FLAGS = {"partition_attn.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+_ATTN_FLAGS = ["-fno-honor-nans", "-mno-amdgpu-ieee"]
+SOURCE_FLAGS = {"partition_attn.hip": _ATTN_FLAGS, "partition_attn_fp8.hip": _ATTN_FLAGS,
+                "partition_attn_grouped.hip": _ATTN_FLAGS}
 
 # Packed fp32 VALU instructions are kept out of the device code on purpose: hipcc
 # only emits them from ordinary float code, and the kernels do not need them.
@@ -54,7 +57,7 @@ def _run(cmd, verbose):
         print(err, file=sys.stderr)
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
+def build(verbose: bool = False, jobs: int = 8) -> str:
     """Compile every source and link the shared library; returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     cc = hipcc()

@@ -81,12 +81,30 @@ const char* as_last_error(void) { return g_last_error; }
 
 namespace {
 
+// Grid of a grouped launch: (G * B * H units rounded up to a multiple of 8) * query tiles.
+as_status check_grid_grouped(int32_t G, int64_t B, int64_t H, int64_t Sq, int64_t D) {
+  const int64_t bq = as::attn_bf16_rows_per_block((int)D);
+  const int64_t units = ((int64_t)G * B * H + 7) / 8 * 8;
+  if (units * ((Sq + bq - 1) / bq) > 0x7fffffff) return fail(AS_ERR_UNSUPPORTED, "grid too large");
+  return AS_OK;
+}
+
+// The grouped variant's extra arguments (as_partition_attn_grouped).
+struct Grouping {
+  const int32_t* starts;
+  int32_t G;
+  const float* fold_out;
+  const float* fold_lse;
+  float* part_lse;
+};
+
 as_status attn_impl(const void* q, const void* k, const void* v, as_dtype dtype,
                     int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
                     const int64_t q_stride[3], const int64_t kv_stride[3],
                     const int32_t* kv_ranges, int32_t P, float scale, as_dtype state_dtype,
                     void* out, float* lse, hipStream_t stream,
-                    bool qk_fp8 = false, const float* q_scale = nullptr, const float* k_scale = nullptr) {
+                    bool qk_fp8 = false, const float* q_scale = nullptr, const float* k_scale = nullptr,
+                    const Grouping* grouping = nullptr) {
   if (dtype != AS_BF16 && dtype != AS_F32) return fail(AS_ERR_INVALID_ARG, "dtype %d is not AS_BF16 or AS_F32", (int)dtype);
   if (state_dtype != AS_BF16 && state_dtype != AS_F32)
     return fail(AS_ERR_INVALID_ARG, "state_dtype %d is not AS_BF16 or AS_F32", (int)state_dtype);
@@ -106,6 +124,22 @@ as_status attn_impl(const void* q, const void* k, const void* v, as_dtype dtype,
     return fail(AS_ERR_UNSUPPORTED, "%s path supports D in {64, 128}, got %lld", qk_fp8 ? "fp8" : "bf16", (long long)D);
   if (dtype == AS_F32 && (D % 4 != 0 || D > 128))
     return fail(AS_ERR_UNSUPPORTED, "f32 path supports D a multiple of 4 up to 128, got %lld", (long long)D);
+  // outputs: P partition states, or G group states (grouped)
+  int64_t n_states = P;
+  if (grouping) {
+    const Grouping& g = *grouping;
+    if (P < 1) return fail(AS_ERR_INVALID_ARG, "grouped launches need P >= 1");
+    if (g.G < 1 || g.G > AS_MAX_PARTITIONS) return fail(AS_ERR_INVALID_ARG, "G=%d outside [1, %d]", g.G, AS_MAX_PARTITIONS);
+    if (!g.starts) return fail(AS_ERR_INVALID_ARG, "group_starts is NULL");
+    if (g.starts[0] != 0 || g.starts[g.G] != P)
+      return fail(AS_ERR_INVALID_ARG, "group_starts must run from 0 to P=%d", P);
+    for (int32_t i = 0; i < g.G; ++i)
+      if (g.starts[i + 1] < g.starts[i]) return fail(AS_ERR_INVALID_ARG, "group_starts decreases at %d", i);
+    if ((g.fold_out == nullptr) != (g.fold_lse == nullptr))
+      return fail(AS_ERR_INVALID_ARG, "fold_out and fold_lse must both be given or both be NULL");
+    if (state_dtype != AS_F32) return fail(AS_ERR_INVALID_ARG, "grouped launches write float32 states");
+    n_states = g.G;
+  }
   if (B == 0 || H == 0 || Sq == 0 || P == 0) return ok();
   if (B > 65535 || H > 65535 || B * H > 65535) return fail(AS_ERR_UNSUPPORTED, "B*H=%lld exceeds 65535", (long long)mul3(B, H));
   if (Sq > 0x7fffffff || Skv > 0x7fffffff) return fail(AS_ERR_UNSUPPORTED, "sequence length exceeds 2^31-1");
@@ -139,17 +173,34 @@ as_status attn_impl(const void* q, const void* k, const void* v, as_dtype dtype,
   const int64_t q_bytes = extent_bytes(B, H, Sq, D, q_stride, qesz);
   const int64_t k_bytes = Skv > 0 ? extent_bytes(B, H, Skv, D, kv_stride, kesz) : 0;
   const int64_t v_bytes = Skv > 0 ? extent_bytes(B, H, Skv, D, kv_stride, esz) : 0;
-  const int64_t out_bytes = mul3(P, rows, D * (state_dtype == AS_BF16 ? 2 : 4));
-  const int64_t lse_bytes = mul3(P, rows, 4);
+  const int64_t out_bytes = mul3(n_states, rows, D * (state_dtype == AS_BF16 ? 2 : 4));
+  const int64_t lse_bytes = mul3(n_states, rows, 4);
   if (q_bytes < 0 || k_bytes < 0 || v_bytes < 0 || out_bytes < 0 || lse_bytes < 0)
     return fail(AS_ERR_UNSUPPORTED, "tensor extents overflow 64-bit byte counts");
   if (overlap(out, (size_t)out_bytes, lse, (size_t)lse_bytes)) return fail(AS_ERR_INVALID_ARG, "out and lse overlap");
-  const void* ins[3] = {q, k, v};
-  const int64_t in_bytes[3] = {q_bytes, k_bytes, v_bytes};
-  for (int j = 0; j < 3; ++j)
+  const void* ins[5] = {q, k, v, nullptr, nullptr};
+  int64_t in_bytes[5] = {q_bytes, k_bytes, v_bytes, 0, 0};
+  const float* part_lse = nullptr;
+  const size_t part_bytes = (size_t)(P * rows) * 4;
+  if (grouping) {
+    const Grouping& g = *grouping;
+    if (g.fold_out && (!aligned(g.fold_out, 16) || !aligned(g.fold_lse, 4)))
+      return fail(AS_ERR_INVALID_ARG, "fold_out must be 16-byte and fold_lse 4-byte aligned");
+    if (g.part_lse && !aligned(g.part_lse, 4)) return fail(AS_ERR_INVALID_ARG, "part_lse must be 4-byte aligned");
+    ins[3] = g.fold_out;
+    in_bytes[3] = rows * D * 4;
+    ins[4] = g.fold_lse;
+    in_bytes[4] = rows * 4;
+    part_lse = g.part_lse;
+    if (overlap(part_lse, part_bytes, out, (size_t)out_bytes) || overlap(part_lse, part_bytes, lse, (size_t)lse_bytes))
+      return fail(AS_ERR_INVALID_ARG, "part_lse overlaps out or lse");
+  }
+  for (int j = 0; j < 5; ++j)
     if (overlap(out, (size_t)out_bytes, ins[j], (size_t)in_bytes[j]) ||
-        overlap(lse, (size_t)lse_bytes, ins[j], (size_t)in_bytes[j]))
-      return fail(AS_ERR_INVALID_ARG, "out or lse overlaps input %c", "qkv"[j]);
+        overlap(lse, (size_t)lse_bytes, ins[j], (size_t)in_bytes[j]) ||
+        overlap(part_lse, part_bytes, ins[j], (size_t)in_bytes[j]))
+      return fail(AS_ERR_INVALID_ARG, "an output overlaps input %s", j < 3 ? (j == 0 ? "q" : j == 1 ? "k" : "v")
+                                                                      : j == 3 ? "fold_out" : "fold_lse");
 
   as::AttnArgs a;
   memset(&a, 0, sizeof(a));
@@ -166,6 +217,41 @@ as_status attn_impl(const void* q, const void* k, const void* v, as_dtype dtype,
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   for (int32_t i = 0; i < 2 * P; ++i) a.ranges[i] = kv_ranges[i];
 
+  if (grouping) {
+    // The kernel walks the non-empty partitions only: pack them in group order and keep
+    // each one's index for its LSE; the LSE of an empty partition is -inf.
+    const as_status gs = check_grid_grouped(grouping->G, B, H, Sq, D);
+    if (gs != AS_OK) return gs;
+    a.G = grouping->G;
+    a.fold_out = grouping->fold_out;
+    a.fold_lse = grouping->fold_lse;
+    a.part_lse = grouping->part_lse;
+    int32_t packed = 0;
+    for (int32_t g = 0; g < grouping->G; ++g) {
+      a.group_starts[g] = (uint16_t)packed;
+      for (int32_t i = grouping->starts[g]; i < grouping->starts[g + 1]; ++i) {
+        if (kv_ranges[2 * i + 1] > kv_ranges[2 * i]) {
+          a.ranges[2 * packed] = kv_ranges[2 * i];
+          a.ranges[2 * packed + 1] = kv_ranges[2 * i + 1];
+          a.part_index[packed] = (uint16_t)i;
+          ++packed;
+        }
+      }
+    }
+    a.group_starts[grouping->G] = (uint16_t)packed;
+    for (int32_t i = packed; i < P; ++i) a.ranges[2 * i] = a.ranges[2 * i + 1] = 0;
+    a.P = packed;
+    const int bq = as::attn_bf16_rows_per_block((int)D);
+    a.n_qtiles = (int32_t)((Sq + bq - 1) / bq);
+    if (grouping->part_lse) {
+      for (int32_t i = 0; i < P; ++i)
+        if (kv_ranges[2 * i + 1] <= kv_ranges[2 * i]) {
+          const hipError_t e = as::launch_fill_neg_inf(grouping->part_lse + (int64_t)i * rows, rows, stream);
+          if (e != hipSuccess) return hip_status(e, "partition_attn grouped: empty partition LSE");
+        }
+    }
+    return hip_status(as::launch_attn_grouped(a, stream), "partition_attn grouped launch");
+  }
   if (dtype == AS_BF16) {
     const int bq = as::attn_bf16_rows_per_block((int)D);
     a.n_qtiles = (int32_t)((Sq + bq - 1) / bq);
@@ -244,6 +330,21 @@ as_status as_partition_attn_fp8(const void* q, const void* k, const void* v, con
                                 void* out, float* lse, hipStream_t stream) {
   return attn_impl(q, k, v, AS_BF16, B, H, Sq, Skv, D, q_stride, kv_stride, kv_ranges, P, scale, state_dtype, out, lse,
                    stream, true, q_scale, k_scale);
+}
+
+as_status as_partition_attn_grouped(const void* q, const void* k, const void* v, as_dtype dtype,
+                                    const float* q_scale, const float* k_scale, int64_t B, int64_t H,
+                                    int64_t Sq, int64_t Skv, int64_t D, const int64_t q_stride[3],
+                                    const int64_t kv_stride[3], const int32_t* kv_ranges, int32_t P,
+                                    const int32_t* group_starts, int32_t G, float scale, const float* fold_out,
+                                    const float* fold_lse, float* out, float* lse, float* part_lse,
+                                    hipStream_t stream) {
+  if (dtype != AS_BF16 && dtype != AS_FP8_E4M3)
+    return fail(AS_ERR_INVALID_ARG, "dtype %d is not AS_BF16 or AS_FP8_E4M3", (int)dtype);
+  const Grouping g = {group_starts, G, fold_out, fold_lse, part_lse};
+  const bool fp8 = dtype == AS_FP8_E4M3;
+  return attn_impl(q, k, v, AS_BF16, B, H, Sq, Skv, D, q_stride, kv_stride, kv_ranges, P, scale, AS_F32, out, lse,
+                   stream, fp8, fp8 ? q_scale : nullptr, fp8 ? k_scale : nullptr, &g);
 }
 
 as_status as_merge_states(int32_t n, const void* const* outs, const float* const* lses, as_dtype in_dtype,

@@ -28,7 +28,20 @@ struct AttnArgs {
   const float* q_scale;      // [B*H] (qk_fp8 only)
   const float* k_scale;      // [B*H] (qk_fp8 only)
   int32_t ranges[2 * AS_MAX_PARTITIONS];
+  // Grouped launches (as_partition_attn_grouped): `ranges` holds the non-empty
+  // partitions only, packed in group order (P of them); group g holds packed partitions
+  // group_starts[g] .. group_starts[g + 1] - 1 and packed partition k is the caller's
+  // partition part_index[k]; out/lse are [G][B][H][Sq](D).
+  int32_t G;
+  const float* fold_out;     // [B][H][Sq][D], composed into group 0's state, or null
+  const float* fold_lse;     // [B][H][Sq]
+  float* part_lse;           // [caller's P][B][H][Sq] LSE of every partition, or null
+  uint16_t group_starts[AS_MAX_PARTITIONS + 1];
+  uint16_t part_index[AS_MAX_PARTITIONS];
 };
+
+// Sets n floats at p to -inf (the LSE of empty partitions in grouped launches).
+hipError_t launch_fill_neg_inf(float* p, int64_t n, hipStream_t stream);
 
 // k-way composition. Pointer mode (group == 0): inputs outs[k], lses[k], k < n.
 // Batched mode (group > 0, group-wise composition): n = P slices of one
@@ -65,7 +78,9 @@ struct ContribArgs {
 int attn_bf16_rows_per_block(int D);
 int attn_f32_rows_per_block(int D);
 
-hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream);   // bf16 or fp8 q/k (qk_fp8)
+hipError_t launch_attn_fp8(const AttnArgs& a, hipStream_t stream);    // fp8 q/k
+hipError_t launch_attn_grouped(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 

@@ -113,6 +113,68 @@ class SelectiveReuse:
         self._timed("contrib_step", self._contribution, self.step_lse, self.step_weights, self.step_scores)
         return self.result_out, self.result_lse
 
+    # ------------------------------------------------------------------ #
+    # Grouped launches: the partition-attention epilogue composes the states
+    # ------------------------------------------------------------------ #
+
+    def grouped_layout(self, far_group: int) -> Tuple[List[int], List[int]]:
+        """Partition order and group starts of a grouped anchor: the far partitions in runs of
+        `far_group` (composed in the kernel; long groups first), then every near partition alone."""
+        order = list(self.far) + list(self.near)
+        starts = list(range(0, len(self.far), far_group)) + [len(self.far) + i for i in range(len(self.near) + 1)]
+        return order, starts
+
+    def anchor_grouped(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, far_group: int = 4,
+                       scales=None) -> None:
+        """Step t with grouped launches: one launch gives the composed state of every run of
+        `far_group` far partitions, the state of every near partition and the LSE of all partitions
+        (weights from those); the cached state composes the far groups' states. The partition order
+        of the weights and scores is grouped_layout's (far partitions first)."""
+        order, starts = self.grouped_layout(far_group)
+        G = len(starts) - 1
+        n_far_groups = G - len(self.near)
+        key = (far_group,)
+        if getattr(self, "_grouped_key", None) != key:
+            shape = self.state_out.shape[1:]
+            self.group_out = torch.empty((G,) + tuple(shape), dtype=torch.float32, device=self.state_out.device)
+            self.group_lse = torch.empty((G,) + tuple(self.state_lse.shape[1:]), dtype=torch.float32,
+                                         device=self.state_out.device)
+            self._grouped_key = key
+        fp8 = scales is not None
+        self._timed("attn_anchor_grouped", _native.partition_attn_grouped, q, k, v, [self.ranges[i] for i in order],
+                    starts, self.scale, None, True, scales[0] if fp8 else None, scales[1] if fp8 else None,
+                    self.group_out, self.group_lse, self.state_lse)
+        self._timed("contrib_anchor", self._contribution, self.state_lse, self.anchor_weights, self.anchor_scores)
+        self._timed("merge_cached_grouped", _native.merge, [self.group_out[g] for g in range(n_far_groups)],
+                    [self.group_lse[g] for g in range(n_far_groups)], out=self.cached_out, lse=self.cached_lse)
+
+    def step_grouped(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, near_group: int | None = None,
+                     scales=None) -> Tuple[torch.Tensor, torch.Tensor]:
+        """Step t+1 with grouped launches: the near partitions in runs of `near_group` (all of them
+        by default), the cached state composed into the first group's result in the kernel; more
+        than one group is then composed by as_merge. Every near partition's LSE goes to the weights."""
+        nf = len(self.near)
+        ng = nf if near_group is None else near_group
+        starts = list(range(0, nf, ng)) + [nf]
+        G = len(starts) - 1
+        if getattr(self, "_step_group_key", None) != G:
+            self.step_group_out = torch.empty((G,) + tuple(self.result_out.shape), dtype=torch.float32,
+                                              device=self.result_out.device)
+            self.step_group_lse = torch.empty((G,) + tuple(self.result_lse.shape), dtype=torch.float32,
+                                              device=self.result_out.device)
+            self._step_group_key = G
+        fp8 = scales is not None
+        dst_out, dst_lse = (self.result_out[None], self.result_lse[None]) if G == 1 else (self.step_group_out,
+                                                                                          self.step_group_lse)
+        self._timed("attn_fresh_grouped", _native.partition_attn_grouped, q, k, v,
+                    [self.ranges[i] for i in self.near], starts, self.scale, (self.cached_out, self.cached_lse), True,
+                    scales[0] if fp8 else None, scales[1] if fp8 else None, dst_out, dst_lse, self.step_lse[:nf])
+        if G > 1:
+            self._timed("merge_step_grouped", _native.merge, list(self.step_group_out), list(self.step_group_lse),
+                        out=self.result_out, lse=self.result_lse)
+        self._timed("contrib_step", self._contribution, self.step_lse, self.step_weights, self.step_scores)
+        return self.result_out, self.result_lse
+
     def plan_anchor(self) -> None:
         """Planner statistics of the anchor step: ||OUT(i)|| per partition and the global weights w(i)."""
         self._timed("plan_norms_anchor", _native.state_norms, self.state_out.view(self.P, -1),

@@ -1,0 +1,169 @@
+"""GPU parity of grouped launches (as_partition_attn_grouped): the composed state of every group
+of consecutive partitions, every partition's LSE and a state folded into group 0, against the
+fp64 oracle (partition states composed by oracle.merge), through the C ABI.
+
+Tolerances as for single-partition launches: bf16 inputs 2e-2 on OUT and 1e-3 on LSE."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sequence_dit_amd import _native as N
+from sequence_dit_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL, LSE_TOL = 2e-2, 1e-3
+DEV = "cuda:0"
+
+
+def note(msg):
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    N.lib()
+
+
+def dev(t):
+    return t.to(DEV)
+
+
+def oracle_groups(o, l, starts):
+    """Composition of partitions starts[g] .. starts[g+1]-1 for every group g (empty group: (0, -inf))."""
+    outs, lses = [], []
+    for g in range(len(starts) - 1):
+        s, e = starts[g], starts[g + 1]
+        if e > s:
+            mo, ml = oracle.merge(o[s:e], l[s:e])
+        else:
+            mo, ml = np.zeros(o.shape[1:]), np.full(l.shape[1:], -np.inf)
+        outs.append(mo)
+        lses.append(ml)
+    return np.stack(outs), np.stack(lses)
+
+
+def check(out, lse, o_ref, l_ref, what, out_tol=OUT_TOL, lse_tol=LSE_TOL):
+    out = out.detach().cpu().double().numpy()
+    lse = lse.detach().cpu().double().numpy()
+    empty = np.isneginf(l_ref)
+    assert np.array_equal(np.isneginf(lse), empty), f"{what}: -inf pattern differs"
+    assert np.all(out[empty] == 0), f"{what}: empty state OUT is not 0"
+    assert np.all(np.isfinite(out)), f"{what}: non-finite OUT"
+    eo = np.abs(out - o_ref).max() if out.size else 0.0
+    el = np.abs(lse[~empty] - l_ref[~empty]).max() if (~empty).any() else 0.0
+    assert eo <= out_tol, f"{what}: OUT max-abs error {eo:.3e} > {out_tol}"
+    assert el <= lse_tol, f"{what}: LSE max-abs error {el:.3e} > {lse_tol}"
+    return eo, el
+
+
+# ragged, single-key, empty and overlapping ranges; groups of 3, 0 (empty), 2 and 4 partitions
+RANGES = [(0, 200), (200, 201), (201, 201), (201, 777), (777, 1000), (100, 300), (0, 1000), (5, 5), (333, 334)]
+STARTS = [0, 3, 3, 5, 9]
+
+
+def decoded(w):
+    qd = oracle.fp8.dequantize(w.q8.view(torch.uint8).numpy(), w.q_scale.numpy())
+    kd = oracle.fp8.dequantize(w.k8.view(torch.uint8).numpy(), w.k_scale.numpy())
+    return qd, kd
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("D", [128, 64])
+def test_grouped_states_and_partition_lse(D, fp8):
+    note(f"grouped D={D} fp8={fp8} B=2 H=3 Sq=300 Skv=1000 P={len(RANGES)} groups={STARTS}")
+    if fp8:
+        w = inputs.small_case_fp8(120 + D, 2, 3, 300, 1000, D, RANGES)
+        out, lse, plse = N.partition_attn_grouped(dev(w.q8), dev(w.k8), dev(w.v), w.ranges, STARTS, w.scale,
+                                                  q_scale=dev(w.q_scale), k_scale=dev(w.k_scale))
+        qd, kd = decoded(w)
+        o_ref, l_ref = oracle.partition_states(qd, kd, w.v, w.ranges, w.scale)
+    else:
+        w = inputs.small_case(110 + D, 2, 3, 300, 1000, D, RANGES)
+        out, lse, plse = N.partition_attn_grouped(dev(w.q), dev(w.k), dev(w.v), w.ranges, STARTS, w.scale)
+        o_ref, l_ref = oracle.partition_states(w.q, w.k, w.v, w.ranges, w.scale)
+    torch.cuda.synchronize()
+    # every partition's LSE, in the caller's order, -inf for the empty ones
+    got = plse.cpu().double().numpy()
+    fin = np.isfinite(l_ref)
+    assert np.array_equal(np.isneginf(got), ~fin)
+    assert np.abs(got[fin] - l_ref[fin]).max() <= LSE_TOL
+    g_out, g_lse = oracle_groups(o_ref, l_ref, STARTS)
+    check(out, lse, g_out, g_lse, f"grouped D={D} fp8={fp8}")
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_grouped_fold_into_group_zero(D):
+    """A given state composed into group 0's result (as the cached state at a reuse step)."""
+    ranges = inputs.equal_ranges(1000, 5)
+    starts = [0, 2, 5]
+    w = inputs.small_case(130 + D, 1, 2, 257, 1000, D, ranges)
+    g = np.random.default_rng(D)
+    fo = g.standard_normal((1, 2, 257, D)).astype(np.float32)
+    fl = (g.standard_normal((1, 2, 257)) * 2 + 5).astype(np.float32)
+    fl[0, 0, :7] = -np.inf   # rows where the given state is empty
+    fo[0, 0, :7] = 0
+    note(f"grouped fold D={D}")
+    out, lse, plse = N.partition_attn_grouped(dev(w.q), dev(w.k), dev(w.v), ranges, starts, w.scale,
+                                              fold=(dev(torch.from_numpy(fo)), dev(torch.from_numpy(fl))))
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.partition_states(w.q, w.k, w.v, ranges, w.scale)
+    r0 = oracle.merge(np.concatenate([o_ref[0:2], fo[None]]), np.concatenate([l_ref[0:2], fl[None]]))
+    r1 = oracle.merge(o_ref[2:5], l_ref[2:5])
+    check(out[0], lse[0], r0[0], r0[1], f"fold group 0 D={D}")
+    check(out[1], lse[1], r1[0], r1[1], f"group 1 D={D}")
+
+
+def test_grouped_fold_into_empty_group_is_the_given_state():
+    """An empty group 0 with a given state returns that state bit for bit."""
+    ranges = [(0, 300), (300, 300)]
+    w = inputs.small_case(141, 1, 2, 100, 300, 128, ranges)
+    g = np.random.default_rng(3)
+    fo = torch.from_numpy(g.standard_normal((1, 2, 100, 128)).astype(np.float32))
+    fl = torch.from_numpy((g.standard_normal((1, 2, 100)) + 3).astype(np.float32))
+    note("grouped fold into an empty group")
+    out, lse, plse = N.partition_attn_grouped(dev(w.q), dev(w.k), dev(w.v), ranges, [0, 1, 2], w.scale,
+                                              fold=(dev(fo), dev(fl)))
+    out2, lse2, _ = N.partition_attn_grouped(dev(w.q), dev(w.k), dev(w.v), [(300, 300), (0, 300)], [0, 1, 2],
+                                             w.scale, fold=(dev(fo), dev(fl)))
+    torch.cuda.synchronize()
+    assert torch.equal(out2[0].cpu(), fo) and torch.equal(lse2[0].cpu(), fl)
+    assert torch.all(torch.isneginf(plse[1]))
+    o_ref, l_ref = oracle.partition_states(w.q, w.k, w.v, ranges, w.scale)
+    r0 = oracle.merge(np.stack([o_ref[0], fo.double().numpy()]), np.stack([l_ref[0], fl.double().numpy()]))
+    check(out[0], lse[0], r0[0], r0[1], "fold into the first group")
+    check(out[1], lse[1], np.zeros_like(o_ref[1]), np.full_like(l_ref[1], -np.inf), "empty second group")
+
+
+def test_grouped_single_partition_groups_equal_ungrouped_launch():
+    """Groups of one partition are the single-partition states: same arithmetic up to the order
+    of the row-sum additions."""
+    ranges = [(0, 700), (13, 650), (650, 700), (2, 3)]
+    w = inputs.small_case(150, 2, 2, 260, 700, 128, ranges)
+    note("grouped with groups of one vs single-partition launch")
+    out, lse, plse = N.partition_attn_grouped(dev(w.q), dev(w.k), dev(w.v), ranges, [0, 1, 2, 3, 4], w.scale)
+    o1, l1 = N.partition_attn(dev(w.q), dev(w.k), dev(w.v), ranges, w.scale)
+    torch.cuda.synchronize()
+    assert (out - o1).abs().max().item() <= 1e-5
+    assert (lse - l1).abs().max().item() <= 1e-5 and (plse - l1).abs().max().item() <= 1e-5
+
+
+@pytest.mark.parametrize("cfg,group", [(2, 2), (3, 4)])
+def test_grouped_full_size_image_and_video(cfg, group):
+    """The image and video DiT workloads at full size in groups, every element."""
+    w = inputs.make(cfg)
+    starts = list(range(0, w.P, group)) + [w.P]
+    note(f"grouped full size {w.name}, groups of {group}")
+    out, lse, plse = N.partition_attn_grouped(dev(w.q), dev(w.k), dev(w.v), w.ranges, starts, w.scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.partition_states(w.q, w.k, w.v, w.ranges, w.scale)
+    g_out, g_lse = oracle_groups(o_ref, l_ref, starts)
+    eo, el = check(out, lse, g_out, g_lse, f"config {cfg} grouped")
+    assert np.abs(plse.cpu().double().numpy() - l_ref).max() <= LSE_TOL
+    note(f"config {cfg} grouped: OUT max-abs {eo:.3e}, LSE max-abs {el:.3e}")

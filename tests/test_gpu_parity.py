@@ -799,3 +799,31 @@ def test_full_size_long_video_fp8(reuse_workload):
     fp8_full_size_check(w, q8, k8, qs, ks, [0, 11, 23], list(range(w.Sq)), "long video fp8")
     del w.v_dev
 
+
+@pytest.mark.parametrize("near_group", [None, 2])
+def test_full_size_grouped_selective_reuse(reuse_workload, reuse_reference, near_group):
+    """The selective-reuse step with grouped launches at full size (every row of three heads): the
+    anchor composes the far partitions in groups of 4 inside the attention launch, the next step
+    folds the cached state into the near partitions' composed state (in one group, or in groups of
+    two and then as_merge)."""
+    w = reuse_workload
+    note(f"full size grouped selective reuse, near_group={near_group}")
+    runner = SelectiveReuse(w.B, w.H, w.Sq, w.D, w.ranges, w.near, DEV, w.scale)
+    q, k, v = to_dev(w.q), to_dev(w.k), to_dev(w.v)
+    runner.anchor_grouped(q, k, v, far_group=4)
+    del q, k, v
+    r_out, r_lse = runner.step_grouped(to_dev(w.q1), to_dev(w.k1), to_dev(w.v1), near_group=near_group)
+    torch.cuda.synchronize()
+    o_t, l_t, o_t1, l_t1 = reuse_reference
+    heads, rs = REUSE_HEADS, list(range(w.Sq))
+    ref_out, ref_lse, c_out, c_lse = oracle.selective_reuse(o_t, l_t, o_t1, l_t1, w.near)
+    check_states(runner.cached_out[:, heads][:, :, rs], runner.cached_lse[:, heads][:, :, rs], c_out, c_lse,
+                 BF16_OUT, BF16_LSE, "grouped cached state")
+    check_states(r_out[:, heads][:, :, rs], r_lse[:, heads][:, :, rs], ref_out, ref_lse, BF16_OUT, BF16_LSE,
+                 "grouped reuse result")
+    # every partition's LSE at the anchor, in the grouped order, and the near ones at the next step
+    order, _ = runner.grouped_layout(4)
+    got = runner.state_lse[:, :, heads].cpu().double().numpy()
+    assert np.abs(got - l_t[order]).max() <= BF16_LSE
+    got1 = runner.step_lse[:len(w.near), :, heads].cpu().double().numpy()
+    assert np.abs(got1 - l_t1[w.near]).max() <= BF16_LSE
