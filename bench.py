@@ -31,7 +31,10 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5000.0
 PEAK_MIXED_TFLOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "partition_attn_traffic.txt")
-ATTN_SOURCES = [os.path.join(ROOT, "sequence_dit_amd", "csrc", f) for f in ("attn_kernel.h", "partition_attn.hip")]
+ATTN_SOURCES = [os.path.join(ROOT, "sequence_dit_amd", "csrc", f)
+                for f in ("attn_kernel.h", "partition_attn.hip", "partition_attn_grouped.hip")]
+# the anchor composes the far partitions in runs of this many inside the attention launch
+FAR_GROUP = 4
 
 
 def log(msg):
@@ -202,32 +205,35 @@ def merge_sweep(N, torch, dev, state_out, state_lse, far, near_plus_cached, reps
     return res
 
 
-def grouped_sweep(runner, N, torch, q, k, v, q1, k1, v1, steps, ms_step, step_flops, attn_flops):
-    """The reuse step on grouped launches: the anchor composes the far partitions in groups of 4 inside
-    the attention epilogue (then a 7-way merge instead of the 28-way one), the next step folds the
-    cached state into the near partitions' composed state in one launch (near_group None) or in two
-    groups plus a 3-way merge (near_group 2). Whole step timed like the main one, and per call."""
+def variant_sweep(runner, torch, q, k, v, q1, k1, v1, steps, ms_step, step_flops, attn_flops):
+    """The reuse step in other arrangements of the same work, each timed as a whole step like the
+    main one and per call: every launch ungrouped (the anchor writes all 32 partition states, then
+    the 28-way composition of the far ones), and grouped launches at the next step too (the cached
+    state folded into the near partitions' composed state in one launch, or in two groups plus a
+    3-way merge)."""
     res = {}
-    for ng in (None, 2):
-        tag = "" if ng is None else f"_near{ng}"
+    anchor_flops = attn_flops["attn_anchor_grouped"]
+    variants = (("ungrouped", lambda: (runner.anchor(q, k, v), runner.step(q1, k1, v1))),
+                ("grouped_both", lambda: (runner.anchor_grouped(q, k, v, FAR_GROUP),
+                                          runner.step_grouped(q1, k1, v1, None))),
+                ("grouped_both_near2", lambda: (runner.anchor_grouped(q, k, v, FAR_GROUP),
+                                                runner.step_grouped(q1, k1, v1, 2))))
+    for tag, fn in variants:
         runner.timer = None
-        runner.anchor_grouped(q, k, v, 4)
-        runner.step_grouped(q1, k1, v1, ng)
+        fn()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(steps):
-            runner.anchor_grouped(q, k, v, 4)
-            runner.step_grouped(q1, k1, v1, ng)
+            fn()
         e1.record()
         torch.cuda.synchronize()
         t = e0.elapsed_time(e1) / steps
-        res[f"step_grouped{tag}"] = {"ms": round(t, 4), "TFLOP/s": round(step_flops / t / 1e9, 1),
-                                     "speedup_vs_ungrouped": round(ms_step / t, 3)}
+        res[f"step_{tag}"] = {"ms": round(t, 4), "TFLOP/s": round(step_flops / t / 1e9, 1),
+                              "main_step_speedup_over_it": round(t / ms_step, 3)}
         runner.timer = []
         for _ in range(max(1, steps // 2)):
-            runner.anchor_grouped(q, k, v, 4)
-            runner.step_grouped(q1, k1, v1, ng)
+            fn()
         torch.cuda.synchronize()
         times = {}
         for name, a, b in runner.timer:
@@ -235,11 +241,12 @@ def grouped_sweep(runner, N, torch, q, k, v, q1, k1, v1, steps, ms_step, step_fl
         for name, ts in times.items():
             ms = sum(ts) / len(ts)
             entry = {"ms": round(ms, 4)}
-            base = {"attn_anchor_grouped": "attn_anchor", "attn_fresh_grouped": "attn_fresh"}.get(name)
-            if base:
-                entry["TFLOP/s"] = round(attn_flops[base] / ms / 1e9, 1)
-                entry["frac_mfma"] = round(attn_flops[base] / ms / 1e9 / PEAK_BF16_TFLOPS, 4)
-            res[f"{name}{tag}"] = entry
+            fl = {"attn_anchor": anchor_flops, "attn_anchor_grouped": anchor_flops, "attn_fresh": attn_flops["attn_fresh"],
+                  "attn_fresh_grouped": attn_flops["attn_fresh"]}.get(name)
+            if fl:
+                entry["TFLOP/s"] = round(fl / ms / 1e9, 1)
+                entry["frac_mfma"] = round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4)
+            res[f"{tag}:{name}"] = entry
     runner.timer = None
     return res
 
@@ -252,6 +259,9 @@ def main():
     ap.add_argument("--config", type=int, default=5, choices=[2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=22.0)
+    ap.add_argument("--main-only", action="store_true",
+                    help="time the step only: skip the other kernels, arrangements and shapes reported under "
+                         "`kernels` (for short profiler runs)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy (y = x * 1, fp32) reading and writing this many MiB, "
                          "outside the timed region, to calibrate HBM byte counters")
@@ -288,7 +298,7 @@ def main():
 
     def step():
         if reuse:
-            runner.anchor(q, k, v)
+            runner.anchor_grouped(q, k, v, FAR_GROUP)
             runner.step(q1, k1, v1)
         else:
             runner._timed("attn_anchor", N.partition_attn, q, k, v, w.ranges, w.scale,
@@ -328,24 +338,37 @@ def main():
     rows = w.B * w.H * w.Sq
     state_bytes = rows * (4 * w.D + 4)
     per_key = 4 * w.B * w.H * w.Sq * w.D
-    attn_flops = {"attn_anchor": per_key * sum(e - s for s, e in w.ranges)}
-    attn_bytes = {"attn_anchor": 2 * w.B * w.H * (w.Sq * w.D + 2 * sum(e - s for s, e in w.ranges) * w.D)
-                  + w.P * state_bytes}
+    all_keys = sum(e - s for s, e in w.ranges)
+    anchor_flops = per_key * all_keys
+    attn_flops = {"attn_anchor": anchor_flops}
+    attn_bytes = {"attn_anchor": 2 * w.B * w.H * (w.Sq * w.D + 2 * all_keys * w.D) + w.P * state_bytes}
     merges = {}
     contribs = {"contrib_anchor": w.P}
     if reuse:
+        # the anchor on grouped launches: composed states of the far groups and of each near
+        # partition, plus every partition's LSE
+        _, starts = runner.grouped_layout(FAR_GROUP)
+        n_groups = len(starts) - 1
+        n_far_groups = n_groups - len(near)
+        attn_flops.pop("attn_anchor")
+        attn_bytes.pop("attn_anchor")
+        attn_flops["attn_anchor_grouped"] = anchor_flops
+        attn_bytes["attn_anchor_grouped"] = (2 * w.B * w.H * (w.Sq * w.D + 2 * all_keys * w.D) + n_groups * state_bytes
+                                             + w.P * rows * 4)
         fresh_keys = sum(w.ranges[i][1] - w.ranges[i][0] for i in near)
         attn_flops["attn_fresh"] = per_key * fresh_keys
         attn_bytes["attn_fresh"] = 2 * w.B * w.H * (w.Sq * w.D + 2 * fresh_keys * w.D) + len(near) * state_bytes
-        merges = {"merge_cached": w.P - len(near), "merge_step": len(near) + 1}
+        merges = {"merge_cached_grouped": n_far_groups, "merge_step": len(near) + 1}
         contribs["contrib_step"] = len(near) + 1
     else:
         merges = {"merge_all": w.P}
 
     step_flops = sum(attn_flops.values())
-    attn_ms = sum(sum(times[n]) for n in attn_flops)
-    attn_launches = sum(len(times[n]) for n in attn_flops)
-    attn_total_flops = sum(attn_flops[n] * len(times[n]) for n in attn_flops)
+    # the dominant kernel: the anchor's attention launch (grouped for the reuse workload)
+    dom = "attn_anchor_grouped" if reuse else "attn_anchor"
+    attn_ms = sum(times[dom])
+    attn_launches = len(times[dom])
+    attn_total_flops = attn_flops[dom] * attn_launches
     achieved = attn_total_flops / (attn_ms * 1e-3) / 1e12
     kernels = {}
     for n in attn_flops:
@@ -368,7 +391,7 @@ def main():
     merge_gbps = merge_bytes_total / (merge_ms_total * 1e-3) / 1e9
 
     reuse_quality = None
-    if reuse:
+    if reuse and not args.main_only:
         # quality of the reuse step (outside the timed region): the step's result against full
         # attention at t+1 (all 32 partitions, composed), and the time that full attention takes
         runner.timer = None
@@ -450,7 +473,7 @@ def main():
             ctimes.setdefault(name, []).append(s.elapsed_time(e))
         st16_bytes = rows * (2 * w.D + 4)
         ms = sum(ctimes["attn_anchor_bf16_states"]) / len(ctimes["attn_anchor_bf16_states"])
-        kernels["attn_anchor_bf16_states"] = {"ms": round(ms, 4), "TFLOP/s": round(attn_flops["attn_anchor"] / ms / 1e9, 1)}
+        kernels["attn_anchor_bf16_states"] = {"ms": round(ms, 4), "TFLOP/s": round(anchor_flops / ms / 1e9, 1)}
         for name, by in (("merge_cached_bf16", (len(far) + 1) * st16_bytes),
                          ("compose_groups_g4_bf16", (w.P + G) * st16_bytes)):
             ms = sum(ctimes[name]) / len(ctimes[name])
@@ -472,20 +495,25 @@ def main():
         f_lse = torch.empty((len(near),) + tuple(runner.state_lse.shape[1:]), dtype=torch.float32, device=dev)
 
         def fp8_calls():
+            # the same single-partition launches on bf16 and fp8 q/k, back to back
+            runner._timed("attn_anchor_bf16", N.partition_attn, q, k, v, w.ranges, w.scale,
+                          out=runner.state_out, lse=runner.state_lse)
             runner._timed("attn_anchor_fp8", N.partition_attn_fp8, q8, k8, v, qs8, ks8, w.ranges, w.scale,
                           out=runner.state_out, lse=runner.state_lse)
+            runner._timed("attn_fresh_bf16", N.partition_attn, q1, k1, v1, near_ranges, w.scale,
+                          out=f_out, lse=f_lse)
             runner._timed("attn_fresh_fp8", N.partition_attn_fp8, q18, k18, v1, qs18, ks18, near_ranges, w.scale,
                           out=f_out, lse=f_lse)
 
         # the whole step (anchor + next step, with their compositions and weights) on fp8 q/k
         runner.timer = None
-        runner.anchor(q8, k8, v, (qs8, ks8))
+        runner.anchor_grouped(q8, k8, v, FAR_GROUP, (qs8, ks8))
         runner.step(q18, k18, v1, (qs18, ks18))
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(args.steps):
-            runner.anchor(q8, k8, v, (qs8, ks8))
+            runner.anchor_grouped(q8, k8, v, FAR_GROUP, (qs8, ks8))
             runner.step(q18, k18, v1, (qs18, ks18))
         e1.record()
         torch.cuda.synchronize()
@@ -503,22 +531,28 @@ def main():
         ftimes = {}
         for name, s, e in runner.timer:
             ftimes.setdefault(name, []).append(s.elapsed_time(e))
-        for name, base in (("attn_anchor_fp8", "attn_anchor"), ("attn_fresh_fp8", "attn_fresh")):
+        for name, base, fl in (("attn_anchor_fp8", "attn_anchor_bf16", anchor_flops),
+                               ("attn_fresh_fp8", "attn_fresh_bf16", attn_flops["attn_fresh"])):
             ms = sum(ftimes[name]) / len(ftimes[name])
-            tf = attn_flops[base] / ms / 1e9
+            ms16 = sum(ftimes[base]) / len(ftimes[base])
+            tf = fl / ms / 1e9
             kernels[name] = {"ms": round(ms, 4), "TFLOP/s": round(tf, 1), "frac_mixed_peak": round(tf / PEAK_MIXED_TFLOPS, 4),
-                             "speedup_vs_bf16": round(kernels[base]["ms"] / ms, 3)}
+                             "speedup_vs_bf16": round(ms16 / ms, 3)}
+            kernels[base] = {"ms": round(ms16, 4), "TFLOP/s": round(fl / ms16 / 1e9, 1),
+                             "frac_mfma": round(fl / ms16 / 1e9 / PEAK_BF16_TFLOPS, 4)}
         del q8, k8, q18, k18, f_out, f_lse
 
     traffic = measured_traffic()
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+    roofline = {"kernel": ("attn_bf16_kernel<128, false, false, true> (grouped anchor: 7 groups of 4 far "
+                           "partitions, 4 near ones alone)") if reuse else f"attn_bf16_kernel<{w.D}, false, false>",
+                "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "algorithmic_flops_per_launch": attn_total_flops / attn_launches,
                 "avg_launch_ms": round(attn_ms / attn_launches, 4)}
 
-    if reuse:
-        log("grouped launches (composition in the attention epilogue)")
-        kernels.update(grouped_sweep(runner, N, torch, q, k, v, q1, k1, v1, args.steps, ms_step, step_flops,
+    if reuse and not args.main_only:
+        log("the step with every launch ungrouped, and with grouped launches at both steps")
+        kernels.update(variant_sweep(runner, torch, q, k, v, q1, k1, v1, args.steps, ms_step, step_flops,
                                      attn_flops))
         log("merges warm and cold (32-way, 28-way, 5-way)")
         runner.timer = None

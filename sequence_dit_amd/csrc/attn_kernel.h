@@ -399,6 +399,9 @@ struct Wave {
           p[e + 1] = (__bf16)p1;
         }
         pf[kb][c] = p;
+        // grouped launches: keep the bf16 packing of P in this phase (left alone, the
+        // compiler sinks it past the barrier into the next MFMA phase, next to its use)
+        if (GR) asm volatile("" : "+v"(pf[kb][c]));
       }
     if (GR) {
       const float t = acc0 + acc1;
@@ -410,48 +413,37 @@ struct Wave {
   }
 };
 
-// Grouped launches: walks the key tiles of partitions p0 .. p1 - 1 of the range list in
-// order, one tile per advance(); past the last one, valid() <= 0. The host packs each
-// group's non-empty partitions, so a partition change needs no search. The next
-// partition's range is loaded one partition ahead: the scalar loads are issued at a
-// partition change, and a workgroup barrier (which waits for every outstanding scalar
-// load) therefore waits for them only there, not on every tile. Every field is
-// wave-uniform (scalar registers).
+// Grouped launches: walks the key tiles of the group's partitions in order, one tile per
+// advance(); past the last one, valid() <= 0. The host packs each group's non-empty
+// partitions, and the kernel copies the group's (first key, keys, caller's index)
+// triples to LDS before the first tile, so a partition change reads LDS (in order with
+// the operand reads) instead of issuing scalar loads in the tile loop. The common path
+// of advance() is one compare and two scalar adds. Every field is wave-uniform.
 template <int KB>
 struct TileCursor {
-  const int32_t* rg;   // [P][2] key ranges (packed: every range non-empty)
-  int p, end, last;    // current partition, one past the group's last, the list's last
-  int ks, n, t;        // its first key, its key count, the tile within it
-  int ks1, n1;         // the next partition's first key and key count
-  __device__ __forceinline__ void load_next() {
-    const int q = max(min(p + 1, last), 0);   // in bounds also past the end
-    ks1 = __builtin_amdgcn_readfirstlane(rg[2 * q]);
-    n1 = p + 1 < end ? __builtin_amdgcn_readfirstlane(rg[2 * q + 1]) - ks1 : 0;
+  const int* tab;      // LDS: 3 ints per partition of the group
+  int p, cnt;          // current partition (group-relative), partitions in the group
+  int first, left;     // the current tile's first key, keys from it to the partition's end
+  __device__ __forceinline__ void set(int q) {   // partition q (cnt: past the end)
+    p = q;
+    first = q < cnt ? __builtin_amdgcn_readfirstlane(tab[3 * q]) : 0;
+    left = q < cnt ? __builtin_amdgcn_readfirstlane(tab[3 * q + 1]) : 0;
   }
-  __device__ __forceinline__ void init(const int32_t* ranges, int p0, int p1, int P) {
-    rg = ranges;
-    p = p0 - 1;
-    end = p1;
-    last = P - 1;
-    load_next();
-    p = p0;
-    ks = ks1;
-    n = n1;
-    t = 0;
-    load_next();
+  __device__ __forceinline__ void init(const int* table, int count) {
+    tab = table;
+    cnt = count;
+    set(0);
   }
-  __device__ __forceinline__ int first_key() const { return ks + t * KB; }
-  __device__ __forceinline__ int valid() const { return n - t * KB; }
-  __device__ __forceinline__ bool last_of_partition() const { return (t + 1) * KB >= n; }
+  __device__ __forceinline__ int first_key() const { return first; }
+  __device__ __forceinline__ int valid() const { return left; }
+  __device__ __forceinline__ bool last_of_partition() const { return left <= KB; }
+  __device__ __forceinline__ int index() const { return __builtin_amdgcn_readfirstlane(tab[3 * p + 2]); }
   __device__ __forceinline__ void advance() {
-    if ((t + 1) * KB < n) {
-      ++t;
-    } else if (p < end) {   // next partition (past the end: n = 0 from then on)
-      ++p;
-      ks = ks1;
-      n = n1;
-      t = 0;
-      load_next();
+    if (left > KB) {
+      left -= KB;
+      first += KB;
+    } else if (p < cnt) {
+      set(p + 1);
     }
   }
 };
@@ -487,6 +479,16 @@ struct Stager {
   __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(int first, int rows) const {
     const int bytes = rows > 0 ? (min(rows, KB) - 1) * stride_bytes + row_bytes : 0;
     const uint64_t base = reinterpret_cast<uint64_t>(src + (int64_t)(rows > 0 ? first : 0) * stride_bytes);
+    return make_rsrc(base, bytes);
+  }
+  // Grouped launches: the same without branches (rows <= 0 gives a zero-length range, whose
+  // base address is then never dereferenced).
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at_nb(int first, int rows) const {
+    const int bytes = max((min(rows, KB) - 1) * stride_bytes + row_bytes, 0);
+    const uint64_t base = reinterpret_cast<uint64_t>(src + (int64_t)first * stride_bytes);
+    return make_rsrc(base, bytes);
+  }
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(uint64_t base, int bytes) const {
     // all of it is wave-uniform; readfirstlane keeps the descriptor in SGPRs
     const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base);
     const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32));
@@ -499,7 +501,7 @@ struct Stager {
   }
   // the cursor's tile, then one tile on (grouped launches)
   __device__ __forceinline__ __amdgpu_buffer_rsrc_t next_rsrc() {
-    const __amdgpu_buffer_rsrc_t rs = rsrc_at(cur.first_key(), cur.valid());
+    const __amdgpu_buffer_rsrc_t rs = rsrc_at_nb(cur.first_key(), cur.valid());
     cur.advance();
     return rs;
   }
@@ -567,6 +569,8 @@ void attn_bf16_kernel(const AttnArgs a) {
   static_assert(kQB == 1 && St::KLOADS >= 1 && St::KLOADS <= 4 && St::VUNITS <= St::GT, "tile shape");
   static_assert(!(GROUPED && OUT_BF16), "grouped launches write fp32 states");
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+  // grouped launches: (first key, keys, caller's index) of every partition of the group
+  __shared__ int gtab[GROUPED ? 3 * AS_MAX_PARTITIONS : 1];
 
   int qtile, bh, part;   // part: the partition, or for GROUPED the group
   if constexpr (GROUPED) {
@@ -700,19 +704,24 @@ void attn_bf16_kernel(const AttnArgs a) {
   // a cursor. After the softmax of a partition's last tile its row sum is complete: its
   // LSE is written and the partition sum restarts.
   TileCursor<KB> sc;   // softmax cursor (grouped launches)
-  int p0 = 0, p1 = 0;
   if constexpr (GROUPED) {
     // readfirstlane: the group's bounds and ranges are uniform; without it the code that
     // depends on them would be compiled as divergent
-    p0 = __builtin_amdgcn_readfirstlane(a.group_starts[part]);
-    p1 = __builtin_amdgcn_readfirstlane(a.group_starts[part + 1]);
+    const int p0 = __builtin_amdgcn_readfirstlane(a.group_starts[part]);
+    const int p1 = __builtin_amdgcn_readfirstlane(a.group_starts[part + 1]);
     for (int p = p0; p < p1; ++p) {   // packed ranges: every one non-empty
       const int n_ = __builtin_amdgcn_readfirstlane(a.ranges[2 * p + 1]) - __builtin_amdgcn_readfirstlane(a.ranges[2 * p]);
       T += (n_ + KB - 1) / KB;
     }
+    for (int i = tid; i < p1 - p0; i += kThreads) {
+      gtab[3 * i] = a.ranges[2 * (p0 + i)];
+      gtab[3 * i + 1] = a.ranges[2 * (p0 + i) + 1] - a.ranges[2 * (p0 + i)];
+      gtab[3 * i + 2] = a.part_index[p0 + i];
+    }
+    __syncthreads();
     start_partition(0, 0);   // src = key 0 of this (b, h); tiles come from the cursor
-    st.cur.init(a.ranges, p0, p1, a.P);
-    sc.init(a.ranges, p0, p1, a.P);
+    st.cur.init(gtab, p1 - p0);
+    sc.init(gtab, p1 - p0);
   }
   auto LDK = [&](int tile) __attribute__((always_inline)) {
     if constexpr (GROUPED) st.load_k_from(st.next_rsrc());
@@ -728,7 +737,7 @@ void attn_bf16_kernel(const AttnArgs a) {
       if (sc.last_of_partition()) {
         const float lp = wave_sum_halves(w.lp);
         if (a.part_lse && qrow < a.Sq && half == 0) {
-          const int orig = __builtin_amdgcn_readfirstlane(a.part_index[sc.p]);   // unpacked index
+          const int orig = sc.index();   // the caller's partition index
           a.part_lse[((int64_t)orig * a.B * a.H + bh) * a.Sq + qrow] = (w.m + __log2f(lp)) * 0.69314718055994530942f;
         }
         w.lp = 0.f;
