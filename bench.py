@@ -452,6 +452,11 @@ def main():
         g16 = torch.empty((G,) + tuple(runner.state_out.shape[1:]), dtype=torch.bfloat16, device=dev)
         g16_lse = torch.empty((G,) + tuple(runner.state_lse.shape[1:]), dtype=torch.float32, device=dev)
         far = runner.far
+        # fp8 state payloads (E4M3 codes + one factor per row), the same three calls
+        sshape = tuple(runner.state_out.shape[1:])
+        st8 = N.Fp8States.empty(w.P, sshape, dev)
+        c8 = N.Fp8States.empty(1, sshape, dev)
+        g8 = N.Fp8States.empty(G, sshape, dev)
 
         def compact_calls():
             runner._timed("attn_anchor_bf16_states", N.partition_attn_states, q, k, v, w.ranges, w.scale,
@@ -460,6 +465,12 @@ def main():
                           [runner.state_lse[i] for i in far], torch.bfloat16, out=c16, lse=c16_lse)
             runner._timed("compose_groups_g4_bf16", N.compose_groups, st16, runner.state_lse, 4, torch.bfloat16,
                           out=g16, lse=g16_lse)
+            runner._timed("attn_anchor_fp8_states", N.partition_attn_states, q, k, v, w.ranges, w.scale,
+                          N.FP8, out=st8, lse=runner.state_lse)
+            runner._timed("merge_cached_fp8", N.merge_states, [st8[i] for i in far],
+                          [runner.state_lse[i] for i in far], N.FP8, out=c8, lse=c16_lse)
+            runner._timed("compose_groups_g4_fp8", N.compose_groups, st8, runner.state_lse, 4, N.FP8,
+                          out=g8, lse=g16_lse)
 
         runner.timer = None
         compact_calls()
@@ -472,16 +483,20 @@ def main():
         for name, s, e in runner.timer:
             ctimes.setdefault(name, []).append(s.elapsed_time(e))
         st16_bytes = rows * (2 * w.D + 4)
-        ms = sum(ctimes["attn_anchor_bf16_states"]) / len(ctimes["attn_anchor_bf16_states"])
-        kernels["attn_anchor_bf16_states"] = {"ms": round(ms, 4), "TFLOP/s": round(anchor_flops / ms / 1e9, 1)}
+        st8_bytes = N.state_bytes(N.FP8, rows, w.D) + rows * 4
+        for name in ("attn_anchor_bf16_states", "attn_anchor_fp8_states"):
+            ms = sum(ctimes[name]) / len(ctimes[name])
+            kernels[name] = {"ms": round(ms, 4), "TFLOP/s": round(anchor_flops / ms / 1e9, 1)}
         for name, by in (("merge_cached_bf16", (len(far) + 1) * st16_bytes),
-                         ("compose_groups_g4_bf16", (w.P + G) * st16_bytes)):
+                         ("compose_groups_g4_bf16", (w.P + G) * st16_bytes),
+                         ("merge_cached_fp8", (len(far) + 1) * st8_bytes),
+                         ("compose_groups_g4_fp8", (w.P + G) * st8_bytes)):
             ms = sum(ctimes[name]) / len(ctimes[name])
             kernels[name] = {"ms": round(ms, 4), "GB/s": round(by / ms / 1e6, 1),
                              "frac_hbm": round(by / ms / 1e6 / PEAK_HBM_GBPS, 4)}
-        kernels["state_bytes_per_row"] = {"fp32": 4 * w.D + 4, "bf16": 2 * w.D + 4,
-                                          "kv_bytes_per_key_bf16": 4 * w.D}
-        del st16, c16, g16
+        kernels["state_bytes_per_row"] = {"fp32": 4 * w.D + 4, "bf16": 2 * w.D + 4, "fp8": w.D + 8,
+                                          "kv_bytes_per_key_bf16": 4 * w.D, "kv_bytes_per_key_fp8": 2 * w.D}
+        del st16, c16, g16, st8, c8, g8
 
         # fp8 E4M3 queries and keys (per-(b, h) factors; the quantisation is the caller's input
         # preparation and is not timed): the anchor over all partitions and the fresh partitions
@@ -490,6 +505,8 @@ def main():
         k8, ks8 = inputs.quantize_fp8(k)
         q18, qs18 = inputs.quantize_fp8(q1)
         k18, ks18 = inputs.quantize_fp8(k1)
+        v8, vs8 = inputs.quantize_fp8(v)
+        v18, vs18 = inputs.quantize_fp8(v1)
         near_ranges = [w.ranges[i] for i in near]
         f_out = torch.empty((len(near),) + tuple(runner.state_out.shape[1:]), dtype=torch.float32, device=dev)
         f_lse = torch.empty((len(near),) + tuple(runner.state_lse.shape[1:]), dtype=torch.float32, device=dev)
@@ -504,6 +521,10 @@ def main():
                           out=f_out, lse=f_lse)
             runner._timed("attn_fresh_fp8", N.partition_attn_fp8, q18, k18, v1, qs18, ks18, near_ranges, w.scale,
                           out=f_out, lse=f_lse)
+            runner._timed("attn_anchor_fp8qkv", N.partition_attn_fp8_qkv, q8, k8, v8, qs8, ks8, vs8, w.ranges,
+                          w.scale, out=runner.state_out, lse=runner.state_lse)
+            runner._timed("attn_fresh_fp8qkv", N.partition_attn_fp8_qkv, q18, k18, v18, qs18, ks18, vs18,
+                          near_ranges, w.scale, out=f_out, lse=f_lse)
 
         # the whole step (anchor + next step, with their compositions and weights) on fp8 q/k
         runner.timer = None
@@ -520,6 +541,19 @@ def main():
         fp8_step_ms = e0.elapsed_time(e1) / args.steps
         kernels["step_fp8"] = {"ms": round(fp8_step_ms, 4), "TFLOP/s": round(step_flops / fp8_step_ms / 1e9, 1),
                                "speedup_vs_bf16": round(ms_step / fp8_step_ms, 3)}
+        # and on fp8 q/k/v
+        runner.anchor_grouped(q8, k8, v8, FAR_GROUP, (qs8, ks8, vs8))
+        runner.step(q18, k18, v18, (qs18, ks18, vs18))
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            runner.anchor_grouped(q8, k8, v8, FAR_GROUP, (qs8, ks8, vs8))
+            runner.step(q18, k18, v18, (qs18, ks18, vs18))
+        e1.record()
+        torch.cuda.synchronize()
+        ms8 = e0.elapsed_time(e1) / args.steps
+        kernels["step_fp8qkv"] = {"ms": round(ms8, 4), "TFLOP/s": round(step_flops / ms8 / 1e9, 1),
+                                  "speedup_vs_bf16": round(ms_step / ms8, 3)}
 
         runner.timer = None
         fp8_calls()
@@ -532,7 +566,9 @@ def main():
         for name, s, e in runner.timer:
             ftimes.setdefault(name, []).append(s.elapsed_time(e))
         for name, base, fl in (("attn_anchor_fp8", "attn_anchor_bf16", anchor_flops),
-                               ("attn_fresh_fp8", "attn_fresh_bf16", attn_flops["attn_fresh"])):
+                               ("attn_fresh_fp8", "attn_fresh_bf16", attn_flops["attn_fresh"]),
+                               ("attn_anchor_fp8qkv", "attn_anchor_bf16", anchor_flops),
+                               ("attn_fresh_fp8qkv", "attn_fresh_bf16", attn_flops["attn_fresh"])):
             ms = sum(ftimes[name]) / len(ftimes[name])
             ms16 = sum(ftimes[base]) / len(ftimes[base])
             tf = fl / ms / 1e9
@@ -540,11 +576,11 @@ def main():
                              "speedup_vs_bf16": round(ms16 / ms, 3)}
             kernels[base] = {"ms": round(ms16, 4), "TFLOP/s": round(fl / ms16 / 1e9, 1),
                              "frac_mfma": round(fl / ms16 / 1e9 / PEAK_BF16_TFLOPS, 4)}
-        del q8, k8, q18, k18, f_out, f_lse
+        del q8, k8, v8, q18, k18, v18, f_out, f_lse
 
     traffic = measured_traffic()
-    roofline = {"kernel": ("attn_bf16_kernel<128, false, false, true> (grouped anchor: 7 groups of 4 far "
-                           "partitions, 4 near ones alone)") if reuse else f"attn_bf16_kernel<{w.D}, false, false>",
+    roofline = {"kernel": ("attn_bf16_kernel<128, 0, false, true, false> (grouped anchor: 7 groups of 4 far "
+                           "partitions, 4 near ones alone)") if reuse else f"attn_bf16_kernel<{w.D}, 0, false, false, false>",
                 "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "algorithmic_flops_per_launch": attn_total_flops / attn_launches,

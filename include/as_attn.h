@@ -51,8 +51,9 @@ typedef enum {
 typedef enum {
   AS_BF16 = 0,     /* bfloat16 Q/K/V: QK^T and PV on bf16 MFMA, fp32 accumulation and softmax */
   AS_F32 = 1,      /* float32 Q/K/V: fp32 arithmetic throughout (accuracy path) */
-  AS_FP8_E4M3 = 2  /* as_partition_attn_grouped only: fp8 E4M3 Q/K codes with per-(b, h)
-                      factors, bfloat16 V (as for as_partition_attn_fp8) */
+  AS_FP8_E4M3 = 2  /* as an input dtype (as_partition_attn_grouped): fp8 E4M3 Q/K codes with
+                      per-(b, h) factors (as for as_partition_attn_fp8); as a state dtype: an
+                      fp8 state payload (see "Compact states" below) */
 } as_dtype;
 
 #define AS_MAX_PARTITIONS 256 /* partitions per as_partition_attn call */
@@ -119,16 +120,41 @@ as_status as_merge(int32_t n, const float* const* outs, const float* const* lses
  *   state is about half the size of the KV it summarises, and composed states can
  *   be merged into coarser groups under memory pressure; the free-parameter ledger
  *   gives the group size g (4, 8 or 16 explored).
- * A state's OUT may be stored as float32 (AS_F32) or bfloat16 (AS_BF16, rounded to
- * nearest even); LSE is always float32. A bf16 state of D = 128 takes 2D + 4 = 260
- * bytes per query row against 516 for fp32. All arithmetic is fp32 either way.
+ * A state's OUT may be stored as float32 (AS_F32), bfloat16 (AS_BF16, rounded to
+ * nearest even) or as an fp8 state payload (AS_FP8_E4M3); LSE is always float32. A bf16
+ * state of D = 128 takes 2D + 4 = 260 bytes per query row against 516 for fp32; an fp8
+ * one D + 8 = 136. All arithmetic is fp32 whatever the storage.
+ *
+ * fp8 state payload (sources: the FastUSP page (mlsanity), abstract: attention traffic
+ * quantised to FP8; its prior work, "FP8 Formats for Deep Learning", defines E4M3): the
+ * OUT of a state of `rows` rows of D is one byte block of as_state_bytes(AS_FP8_E4M3,
+ * rows, D) = rows*D + 16*ceil(4*rows/16) bytes:
+ *   codes    uint8 [rows][D] at byte 0: OCP E4M3 ("e4m3fn") codes, row-major;
+ *   factors  float32 [rows] at byte rows*D (16-byte aligned when D % 16 == 0);
+ * element (r, d) stands for decode(codes[r][d]) * factors[r]. Writers set
+ * factors[r] = amax_r / 448 with amax_r = max_d |OUT[r][d]| (the fp32 value before
+ * storage) and codes[r][d] = E4M3 of OUT[r][d] * (448 / amax_r) rounded to nearest even
+ * (clamped to +-448), both quotients rounded float32; a zero row (an empty state included)
+ * has codes 0 and factor 0. A block of n fp8 states (P partitions, G groups) is n payloads
+ * back to back, payload i at byte i * as_state_bytes(AS_FP8_E4M3, rows, D). fp8 states
+ * need D in {32, 64, 128, 256} (attention: 64 or 128).
  */
+
+/*
+ * as_state_bytes - bytes of one state's OUT storage: rows*D*4 (AS_F32), rows*D*2
+ * (AS_BF16) or the fp8 payload size above (AS_FP8_E4M3). Returns 0 for an invalid
+ * dtype or sizes (rows < 0, D outside [1, 1024]).
+ */
+size_t as_state_bytes(as_dtype state_dtype, int64_t rows, int64_t D);
 
 /*
  * as_partition_attn_states - as_partition_attn with the OUT storage type chosen
  * by state_dtype (AS_F32 gives exactly as_partition_attn). out is DEVICE
- * [P][B][H][Sq][D] of state_dtype, contiguous, 16-byte aligned; every other
- * argument and rule is as for as_partition_attn.
+ * [P][B][H][Sq][D] of state_dtype, contiguous, 16-byte aligned; for AS_FP8_E4M3 it is a
+ * block of P fp8 payloads of rows = B*H*Sq (row index (b*H + h)*Sq + s), whose codes
+ * and factors are those of the fp32 OUT the call computes. AS_FP8_E4M3 states need
+ * dtype AS_BF16 (else AS_ERR_UNSUPPORTED). Every other argument and rule is as for
+ * as_partition_attn.
  */
 as_status as_partition_attn_states(const void* q, const void* k, const void* v, as_dtype dtype,
                                    int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
@@ -169,6 +195,25 @@ as_status as_partition_attn_fp8(const void* q, const void* k, const void* v, con
                                 void* out, float* lse, hipStream_t stream);
 
 /*
+ * as_partition_attn_fp8_qkv - as_partition_attn_fp8 with fp8 values too: q, k and v all
+ * hold E4M3 codes, and a code of v of batch b and head h stands for code * v_scale[b*H + h].
+ *   Source: the FastUSP page (mlsanity), abstract: the attention traffic, keys and
+ *   values included, quantised to FP8.
+ * The states are those of as_partition_attn on the dequantised Q, K and V. The value codes
+ * are widened to bfloat16 (exactly) for PV; v_scale multiplies OUT at the end.
+ * v_scale    DEVICE float32 [B*H], 4-byte aligned, finite, any sign (not checked: device
+ *            memory).
+ * kv_stride  element (= byte) strides of k and v over (b, h, s), multiples of 16.
+ * Every other argument and rule is as for as_partition_attn_fp8 (state_dtype AS_F32,
+ * AS_BF16 or AS_FP8_E4M3).
+ */
+as_status as_partition_attn_fp8_qkv(const void* q, const void* k, const void* v, const float* q_scale,
+                                    const float* k_scale, const float* v_scale, int64_t B, int64_t H, int64_t Sq,
+                                    int64_t Skv, int64_t D, const int64_t q_stride[3], const int64_t kv_stride[3],
+                                    const int32_t* kv_ranges, int32_t P, float scale, as_dtype state_dtype,
+                                    void* out, float* lse, hipStream_t stream);
+
+/*
  * as_partition_attn_grouped - partition attention whose epilogue composes the states of
  * consecutive partitions. For every group g of the range list (partitions
  * group_starts[g] .. group_starts[g + 1] - 1) it writes the composed state of the group's
@@ -182,9 +227,11 @@ as_status as_partition_attn_fp8(const void* q, const void* k, const void* v, con
  *   into coarser groups).
  *
  * dtype         AS_BF16 (q, k, v bfloat16) or AS_FP8_E4M3 (q, k E4M3 codes with q_scale,
- *               k_scale and strides as for as_partition_attn_fp8; v bfloat16). D is 64
+ *               k_scale and strides as for as_partition_attn_fp8; v bfloat16, or E4M3
+ *               codes when v_scale is given, as for as_partition_attn_fp8_qkv). D is 64
  *               or 128.
- * q_scale, k_scale  as for as_partition_attn_fp8 (AS_FP8_E4M3 only; ignored for AS_BF16).
+ * q_scale, k_scale, v_scale  as for as_partition_attn_fp8 and as_partition_attn_fp8_qkv
+ *               (AS_FP8_E4M3 only; ignored for AS_BF16); v_scale NULL: v is bfloat16.
  * kv_ranges, P  as for as_partition_attn, with 1 <= P <= AS_MAX_PARTITIONS.
  * group_starts  HOST int32 [G + 1] with 0 = group_starts[0] <= ... <= group_starts[G] = P;
  *               1 <= G <= AS_MAX_PARTITIONS; an empty group gives (0, -inf). Groups are
@@ -198,7 +245,8 @@ as_status as_partition_attn_fp8(const void* q, const void* k, const void* v, con
  * rules are as for as_partition_attn.
  */
 as_status as_partition_attn_grouped(const void* q, const void* k, const void* v, as_dtype dtype,
-                                    const float* q_scale, const float* k_scale, int64_t B, int64_t H,
+                                    const float* q_scale, const float* k_scale, const float* v_scale,
+                                    int64_t B, int64_t H,
                                     int64_t Sq, int64_t Skv, int64_t D, const int64_t q_stride[3],
                                     const int64_t kv_stride[3], const int32_t* kv_ranges, int32_t P,
                                     const int32_t* group_starts, int32_t G, float scale, const float* fold_out,
@@ -208,9 +256,12 @@ as_status as_partition_attn_grouped(const void* q, const void* k, const void* v,
 /*
  * as_merge_states - as_merge for states whose OUT is stored as in_dtype, writing an
  * OUT of out_dtype (AS_F32/AS_F32 gives exactly as_merge). outs: HOST array of n
- * DEVICE pointers, each [rows][D] of in_dtype; out: DEVICE [rows][D] of out_dtype.
- * OUT pointers are 16-byte aligned for fp32 and 8-byte aligned for bf16 (a slice of
- * a bf16 block with D a multiple of 4 always is). Other rules as for as_merge.
+ * DEVICE pointers, each [rows][D] of in_dtype (AS_FP8_E4M3: a payload of rows rows);
+ * out: DEVICE [rows][D] of out_dtype (or a payload). OUT pointers are 16-byte aligned
+ * for fp32 and fp8 payloads and 8-byte aligned for bf16 (a slice of a bf16 block with D
+ * a multiple of 4 always is). An fp8 input is read as decode(code) * factor of its row;
+ * an fp8 output is written by the payload rule from the fp32 result. With an fp8 state
+ * D must be 32, 64, 128 or 256 (else AS_ERR_UNSUPPORTED). Other rules as for as_merge.
  */
 as_status as_merge_states(int32_t n, const void* const* outs, const float* const* lses, as_dtype in_dtype,
                           int64_t rows, int64_t D, as_dtype out_dtype, void* out, float* lse, hipStream_t stream);
@@ -221,12 +272,13 @@ as_status as_merge_states(int32_t n, const void* const* outs, const float* const
  * as_merge) into one state per group k, for all G = ceil(P / group) groups in one
  * launch.
  *
- * outs, lses  DEVICE [P][rows][D] of in_dtype (16-byte aligned) and float32 [P][rows]
- *             (as written by as_partition_attn_states).
+ * outs, lses  DEVICE [P][rows][D] of in_dtype (16-byte aligned; AS_FP8_E4M3: P payloads)
+ *             and float32 [P][rows] (as written by as_partition_attn_states).
  * P           1 <= P <= AS_MAX_PARTITIONS.   group: 1 <= group <= AS_MAX_MERGE.
  * rows, D     rows >= 0; D a multiple of 4, 4 <= D <= 1024.
- * out, lse    DEVICE [G][rows][D] of out_dtype (16-byte aligned) and float32 [G][rows];
- *             must not overlap the input blocks.
+ * out, lse    DEVICE [G][rows][D] of out_dtype (16-byte aligned; AS_FP8_E4M3: G payloads)
+ *             and float32 [G][rows]; must not overlap the input blocks.
+ * fp8 states as for as_merge_states.
  */
 as_status as_compose_groups(const void* outs, const float* lses, as_dtype in_dtype, int32_t P, int64_t rows,
                             int64_t D, int32_t group, as_dtype out_dtype, void* out, float* lse, hipStream_t stream);

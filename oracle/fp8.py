@@ -6,6 +6,9 @@ prior work): 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits. Exponent
 field 0 encodes subnormals m/8 * 2^-6; the all-ones exponent with all-ones mantissa
 is NaN and there are no infinities, so the largest finite magnitude is
 1.75 * 2^8 = 448. A code of batch b and head h stands for decode(code) * scale[b, h].
+An fp8 attention state stores its OUT as codes with one factor per row (the FastUSP
+page's FP8-quantised attention traffic, applied to states): element (r, d) stands for
+decode(code[r, d]) * factor[r].
 """
 from __future__ import annotations
 
@@ -32,3 +35,9 @@ def dequantize(codes, scale) -> np.ndarray:
     vals = decode_e4m3(codes)
     s = np.asarray(scale, dtype=np.float64)
     return vals * s[:, :, None, None]
+
+
+def decode_state(codes, factors) -> np.ndarray:
+    """An fp8 state's OUT: codes [..., rows, D] (uint8) and row factors [..., rows] -> float64
+    decode(code) * factor of the code's row."""
+    return decode_e4m3(codes) * np.asarray(factors, dtype=np.float64)[..., None]

@@ -21,14 +21,14 @@ LIB_NAME = "libas_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "partition_attn.hip", "partition_attn_fp8.hip", "partition_attn_grouped.hip", "merge.hip",
+SOURCES = ["api.hip", "partition_attn.hip", "partition_attn_fp8.hip", "partition_attn_fp8v.hip", "partition_attn_grouped.hip", "merge.hip",
            "contribution.hip", "planner.hip"]
 
 # Per-source flags. The attention kernels never see NaN (finite inputs, -inf only
 # as a max/exp operand), so NaN-honouring max and IEEE-mode operand
 # canonicalisation are switched off there: fmaxf becomes a single v_max/v_max3.
 _ATTN_FLAGS = ["-fno-honor-nans", "-mno-amdgpu-ieee"]
-SOURCE_FLAGS = {"partition_attn.hip": _ATTN_FLAGS, "partition_attn_fp8.hip": _ATTN_FLAGS,
+SOURCE_FLAGS = {"partition_attn.hip": _ATTN_FLAGS, "partition_attn_fp8.hip": _ATTN_FLAGS, "partition_attn_fp8v.hip": _ATTN_FLAGS,
                 "partition_attn_grouped.hip": _ATTN_FLAGS}
 
 # Packed fp32 VALU instructions are kept out of the device code on purpose: hipcc

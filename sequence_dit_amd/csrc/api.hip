@@ -63,6 +63,16 @@ int64_t extent_bytes(int64_t n0, int64_t n1, int64_t n2, int64_t D, const int64_
 // small enough that byte counts never overflow.
 constexpr int64_t kMaxRows = (int64_t)1 << 40;
 
+// Storage kind of a state dtype, or -1.
+int out_kind(as_dtype t) {
+  return t == AS_F32 ? as::kOutF32 : t == AS_BF16 ? as::kOutBF16 : t == AS_FP8_E4M3 ? as::kOutFP8 : -1;
+}
+
+// Bytes of one state's OUT of `rows` rows (rows * D <= kMaxRows * 1024 by the callers).
+int64_t state_bytes(as_dtype t, int64_t rows, int64_t D) {
+  return t == AS_FP8_E4M3 ? as::fp8_payload_bytes(rows, D) : rows * D * (t == AS_BF16 ? 2 : 4);
+}
+
 }  // namespace
 
 extern "C" {
@@ -104,10 +114,12 @@ as_status attn_impl(const void* q, const void* k, const void* v, as_dtype dtype,
                     const int32_t* kv_ranges, int32_t P, float scale, as_dtype state_dtype,
                     void* out, float* lse, hipStream_t stream,
                     bool qk_fp8 = false, const float* q_scale = nullptr, const float* k_scale = nullptr,
-                    const Grouping* grouping = nullptr) {
+                    const Grouping* grouping = nullptr, bool v_fp8 = false, const float* v_scale = nullptr) {
   if (dtype != AS_BF16 && dtype != AS_F32) return fail(AS_ERR_INVALID_ARG, "dtype %d is not AS_BF16 or AS_F32", (int)dtype);
-  if (state_dtype != AS_BF16 && state_dtype != AS_F32)
-    return fail(AS_ERR_INVALID_ARG, "state_dtype %d is not AS_BF16 or AS_F32", (int)state_dtype);
+  if (out_kind(state_dtype) < 0)
+    return fail(AS_ERR_INVALID_ARG, "state_dtype %d is not AS_F32, AS_BF16 or AS_FP8_E4M3", (int)state_dtype);
+  if (state_dtype == AS_FP8_E4M3 && dtype == AS_F32)
+    return fail(AS_ERR_UNSUPPORTED, "the f32 path writes AS_F32 or AS_BF16 states");
   if (B < 0 || H < 0 || Sq < 0 || Skv < 0) return fail(AS_ERR_INVALID_ARG, "negative size (B=%lld H=%lld Sq=%lld Skv=%lld)",
                                                        (long long)B, (long long)H, (long long)Sq, (long long)Skv);
   if (D < 1) return fail(AS_ERR_INVALID_ARG, "D=%lld must be positive", (long long)D);
@@ -149,7 +161,9 @@ as_status attn_impl(const void* q, const void* k, const void* v, as_dtype dtype,
   if (qk_fp8 && (!q_scale || !k_scale)) return fail(AS_ERR_INVALID_ARG, "q_scale and k_scale must not be NULL");
   if (qk_fp8 && (!aligned(q_scale, 4) || !aligned(k_scale, 4)))
     return fail(AS_ERR_INVALID_ARG, "q_scale and k_scale must be 4-byte aligned");
-  const int64_t esz = dtype == AS_BF16 ? 2 : 4;   // bytes per v element (the widest input)
+  if (v_fp8 && (!v_scale || !aligned(v_scale, 4))) return fail(AS_ERR_INVALID_ARG, "v_scale must be non-NULL and 4-byte aligned");
+  // bytes per v element (the widest input)
+  const int64_t esz = v_fp8 ? 1 : dtype == AS_BF16 ? 2 : 4;
   // fp8 rows are read 16 bytes at a time: 16 one-byte elements
   const int64_t smul = qk_fp8 ? 16 : dtype == AS_BF16 ? 8 : 4;
   for (int j = 0; j < 3; ++j) {
@@ -173,13 +187,14 @@ as_status attn_impl(const void* q, const void* k, const void* v, as_dtype dtype,
   const int64_t q_bytes = extent_bytes(B, H, Sq, D, q_stride, qesz);
   const int64_t k_bytes = Skv > 0 ? extent_bytes(B, H, Skv, D, kv_stride, kesz) : 0;
   const int64_t v_bytes = Skv > 0 ? extent_bytes(B, H, Skv, D, kv_stride, esz) : 0;
-  const int64_t out_bytes = mul3(n_states, rows, D * (state_dtype == AS_BF16 ? 2 : 4));
+  const int64_t out_bytes = mul3(n_states, state_bytes(state_dtype, rows, D));
   const int64_t lse_bytes = mul3(n_states, rows, 4);
   if (q_bytes < 0 || k_bytes < 0 || v_bytes < 0 || out_bytes < 0 || lse_bytes < 0)
     return fail(AS_ERR_UNSUPPORTED, "tensor extents overflow 64-bit byte counts");
   if (overlap(out, (size_t)out_bytes, lse, (size_t)lse_bytes)) return fail(AS_ERR_INVALID_ARG, "out and lse overlap");
-  const void* ins[5] = {q, k, v, nullptr, nullptr};
-  int64_t in_bytes[5] = {q_bytes, k_bytes, v_bytes, 0, 0};
+  const void* ins[8] = {q, k, v, nullptr, nullptr, q_scale, k_scale, v_scale};
+  const int64_t sbytes = qk_fp8 ? B * H * 4 : 0;
+  int64_t in_bytes[8] = {q_bytes, k_bytes, v_bytes, 0, 0, sbytes, sbytes, v_fp8 ? B * H * 4 : 0};
   const float* part_lse = nullptr;
   const size_t part_bytes = (size_t)(P * rows) * 4;
   if (grouping) {
@@ -195,12 +210,12 @@ as_status attn_impl(const void* q, const void* k, const void* v, as_dtype dtype,
     if (overlap(part_lse, part_bytes, out, (size_t)out_bytes) || overlap(part_lse, part_bytes, lse, (size_t)lse_bytes))
       return fail(AS_ERR_INVALID_ARG, "part_lse overlaps out or lse");
   }
-  for (int j = 0; j < 5; ++j)
+  static const char* const in_names[8] = {"q", "k", "v", "fold_out", "fold_lse", "q_scale", "k_scale", "v_scale"};
+  for (int j = 0; j < 8; ++j)
     if (overlap(out, (size_t)out_bytes, ins[j], (size_t)in_bytes[j]) ||
         overlap(lse, (size_t)lse_bytes, ins[j], (size_t)in_bytes[j]) ||
         overlap(part_lse, part_bytes, ins[j], (size_t)in_bytes[j]))
-      return fail(AS_ERR_INVALID_ARG, "an output overlaps input %s", j < 3 ? (j == 0 ? "q" : j == 1 ? "k" : "v")
-                                                                      : j == 3 ? "fold_out" : "fold_lse");
+      return fail(AS_ERR_INVALID_ARG, "an output overlaps input %s", in_names[j]);
 
   as::AttnArgs a;
   memset(&a, 0, sizeof(a));
@@ -208,10 +223,14 @@ as_status attn_impl(const void* q, const void* k, const void* v, as_dtype dtype,
   a.q_sb = q_stride[0]; a.q_sh = q_stride[1]; a.q_ss = q_stride[2];
   a.k_sb = kv_stride[0]; a.k_sh = kv_stride[1]; a.k_ss = kv_stride[2];
   a.out = out; a.lse = lse;
-  a.out_bf16 = state_dtype == AS_BF16 ? 1 : 0;
+  a.out_kind = out_kind(state_dtype);
   a.qk_fp8 = qk_fp8 ? 1 : 0;
+  a.v_fp8 = v_fp8 ? 1 : 0;
   a.q_scale = q_scale;
   a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.state_rows = rows;
+  a.payload_bytes = state_dtype == AS_FP8_E4M3 ? as::fp8_payload_bytes(rows, D) : 0;
   a.B = (int32_t)B; a.H = (int32_t)H; a.Sq = (int32_t)Sq; a.Skv = (int32_t)Skv; a.D = (int32_t)D; a.P = P;
   a.scale = scale;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
@@ -264,25 +283,36 @@ as_status attn_impl(const void* q, const void* k, const void* v, as_dtype dtype,
   return hip_status(as::launch_attn_f32(a, stream), "partition_attn f32 launch");
 }
 
-bool is_state_dtype(as_dtype t) { return t == AS_F32 || t == AS_BF16; }
+// Checks shared by the composition calls: state dtypes and D.
+as_status check_state_types(as_dtype in_dtype, as_dtype out_dtype, int64_t D) {
+  if (out_kind(in_dtype) < 0 || out_kind(out_dtype) < 0)
+    return fail(AS_ERR_INVALID_ARG, "state dtypes must be AS_F32, AS_BF16 or AS_FP8_E4M3");
+  if (D < 4 || D > 1024 || D % 4) return fail(AS_ERR_INVALID_ARG, "D=%lld must be a multiple of 4 in [4, 1024]", (long long)D);
+  if ((in_dtype == AS_FP8_E4M3 || out_dtype == AS_FP8_E4M3) && D != 32 && D != 64 && D != 128 && D != 256)
+    return fail(AS_ERR_UNSUPPORTED, "fp8 states need D in {32, 64, 128, 256}, got %lld", (long long)D);
+  return AS_OK;
+}
+
+// Alignment of a state's OUT pointer: 16 bytes (fp32, fp8 payloads), 8 (bf16).
+size_t state_align(as_dtype t) { return t == AS_BF16 ? 8 : 16; }
 
 as_status merge_impl(int32_t n, const void* const* outs, const float* const* lses, as_dtype in_dtype,
                      int64_t rows, int64_t D, as_dtype out_dtype, void* out, float* lse, hipStream_t stream) {
-  if (!is_state_dtype(in_dtype) || !is_state_dtype(out_dtype))
-    return fail(AS_ERR_INVALID_ARG, "state dtypes must be AS_F32 or AS_BF16");
+  const as_status ts = check_state_types(in_dtype, out_dtype, D);
+  if (ts != AS_OK) return ts;
   if (n < 1 || n > AS_MAX_MERGE) return fail(AS_ERR_INVALID_ARG, "n=%d outside [1, %d]", n, AS_MAX_MERGE);
   if (rows < 0) return fail(AS_ERR_INVALID_ARG, "rows=%lld is negative", (long long)rows);
-  if (D < 4 || D > 1024 || D % 4) return fail(AS_ERR_INVALID_ARG, "D=%lld must be a multiple of 4 in [4, 1024]", (long long)D);
   if (!outs || !lses) return fail(AS_ERR_INVALID_ARG, "NULL pointer list");
   if (rows == 0) return ok();
   if (rows > kMaxRows) return fail(AS_ERR_UNSUPPORTED, "rows=%lld too large", (long long)rows);
   if (!out || !lse) return fail(AS_ERR_INVALID_ARG, "NULL output pointer");
-  // OUT is read and written 4 elements at a time: 16 bytes of fp32, 8 of bf16
-  const size_t ain = in_dtype == AS_BF16 ? 8 : 16, aout = out_dtype == AS_BF16 ? 8 : 16;
+  // OUT is read and written 4 elements at a time: 16 bytes of fp32, 8 of bf16; fp8
+  // payloads up to 16 codes at a time
+  const size_t ain = state_align(in_dtype), aout = state_align(out_dtype);
   if (!aligned(out, aout) || !aligned(lse, 4))
     return fail(AS_ERR_INVALID_ARG, "out must be %zu-byte and lse 4-byte aligned", aout);
-  const size_t in_bytes = (size_t)(rows * D) * (in_dtype == AS_BF16 ? 2 : 4);
-  const size_t out_bytes = (size_t)(rows * D) * (out_dtype == AS_BF16 ? 2 : 4);
+  const size_t in_bytes = (size_t)state_bytes(in_dtype, rows, D);
+  const size_t out_bytes = (size_t)state_bytes(out_dtype, rows, D);
   const size_t lse_bytes = (size_t)rows * 4;
   if (overlap(out, out_bytes, lse, lse_bytes)) return fail(AS_ERR_INVALID_ARG, "out and lse overlap");
   as::MergeArgs a;
@@ -297,7 +327,8 @@ as_status merge_impl(int32_t n, const void* const* outs, const float* const* lse
     a.lses[i] = lses[i];
   }
   a.out = out; a.lse = lse; a.rows = rows; a.n = n; a.D = (int32_t)D;
-  a.in_bf16 = in_dtype == AS_BF16; a.out_bf16 = out_dtype == AS_BF16;
+  a.in_kind = out_kind(in_dtype); a.out_kind = out_kind(out_dtype);
+  a.payload_bytes = as::fp8_payload_bytes(rows, D);
   a.vec2 = D % 8 == 0 && aligned(out, 16);
   for (int32_t i = 0; i < n; ++i) a.vec2 = a.vec2 && aligned(outs[i], 16);
   return hip_status(as::launch_merge(a, stream), "merge launch");
@@ -332,8 +363,17 @@ as_status as_partition_attn_fp8(const void* q, const void* k, const void* v, con
                    stream, true, q_scale, k_scale);
 }
 
+as_status as_partition_attn_fp8_qkv(const void* q, const void* k, const void* v, const float* q_scale,
+                                    const float* k_scale, const float* v_scale, int64_t B, int64_t H, int64_t Sq,
+                                    int64_t Skv, int64_t D, const int64_t q_stride[3], const int64_t kv_stride[3],
+                                    const int32_t* kv_ranges, int32_t P, float scale, as_dtype state_dtype,
+                                    void* out, float* lse, hipStream_t stream) {
+  return attn_impl(q, k, v, AS_BF16, B, H, Sq, Skv, D, q_stride, kv_stride, kv_ranges, P, scale, state_dtype, out, lse,
+                   stream, true, q_scale, k_scale, nullptr, true, v_scale);
+}
+
 as_status as_partition_attn_grouped(const void* q, const void* k, const void* v, as_dtype dtype,
-                                    const float* q_scale, const float* k_scale, int64_t B, int64_t H,
+                                    const float* q_scale, const float* k_scale, const float* v_scale, int64_t B, int64_t H,
                                     int64_t Sq, int64_t Skv, int64_t D, const int64_t q_stride[3],
                                     const int64_t kv_stride[3], const int32_t* kv_ranges, int32_t P,
                                     const int32_t* group_starts, int32_t G, float scale, const float* fold_out,
@@ -342,9 +382,9 @@ as_status as_partition_attn_grouped(const void* q, const void* k, const void* v,
   if (dtype != AS_BF16 && dtype != AS_FP8_E4M3)
     return fail(AS_ERR_INVALID_ARG, "dtype %d is not AS_BF16 or AS_FP8_E4M3", (int)dtype);
   const Grouping g = {group_starts, G, fold_out, fold_lse, part_lse};
-  const bool fp8 = dtype == AS_FP8_E4M3;
+  const bool fp8 = dtype == AS_FP8_E4M3, v8 = fp8 && v_scale != nullptr;
   return attn_impl(q, k, v, AS_BF16, B, H, Sq, Skv, D, q_stride, kv_stride, kv_ranges, P, scale, AS_F32, out, lse,
-                   stream, fp8, fp8 ? q_scale : nullptr, fp8 ? k_scale : nullptr, &g);
+                   stream, fp8, fp8 ? q_scale : nullptr, fp8 ? k_scale : nullptr, &g, v8, v8 ? v_scale : nullptr);
 }
 
 as_status as_merge_states(int32_t n, const void* const* outs, const float* const* lses, as_dtype in_dtype,
@@ -354,31 +394,29 @@ as_status as_merge_states(int32_t n, const void* const* outs, const float* const
 
 as_status as_compose_groups(const void* outs, const float* lses, as_dtype in_dtype, int32_t P, int64_t rows,
                             int64_t D, int32_t group, as_dtype out_dtype, void* out, float* lse, hipStream_t stream) {
-  if (!is_state_dtype(in_dtype) || !is_state_dtype(out_dtype))
-    return fail(AS_ERR_INVALID_ARG, "state dtypes must be AS_F32 or AS_BF16");
+  const as_status ts = check_state_types(in_dtype, out_dtype, D);
+  if (ts != AS_OK) return ts;
   if (P < 1 || P > AS_MAX_PARTITIONS) return fail(AS_ERR_INVALID_ARG, "P=%d outside [1, %d]", P, AS_MAX_PARTITIONS);
   if (group < 1 || group > AS_MAX_MERGE) return fail(AS_ERR_INVALID_ARG, "group=%d outside [1, %d]", group, AS_MAX_MERGE);
   if (rows < 0) return fail(AS_ERR_INVALID_ARG, "rows=%lld is negative", (long long)rows);
-  if (D < 4 || D > 1024 || D % 4) return fail(AS_ERR_INVALID_ARG, "D=%lld must be a multiple of 4 in [4, 1024]", (long long)D);
   if (rows == 0) return ok();
   if (rows > kMaxRows) return fail(AS_ERR_UNSUPPORTED, "rows=%lld too large", (long long)rows);
   if (!outs || !lses || !out || !lse) return fail(AS_ERR_INVALID_ARG, "NULL pointer");
   if (!aligned(outs, 16) || !aligned(out, 16) || !aligned(lses, 4) || !aligned(lse, 4))
     return fail(AS_ERR_INVALID_ARG, "OUT blocks must be 16-byte and LSE blocks 4-byte aligned");
   const int64_t G = (P + group - 1) / group;
-  const size_t ein = in_dtype == AS_BF16 ? 2 : 4, eout = out_dtype == AS_BF16 ? 2 : 4;
-  if (overlap(outs, (size_t)(P * rows * D) * ein, out, (size_t)(G * rows * D) * eout) ||
-      overlap(lses, (size_t)(P * rows) * 4, lse, (size_t)(G * rows) * 4) ||
-      overlap(outs, (size_t)(P * rows * D) * ein, lse, (size_t)(G * rows) * 4) ||
-      overlap(lses, (size_t)(P * rows) * 4, out, (size_t)(G * rows * D) * eout))
+  const size_t in_block = (size_t)(P * state_bytes(in_dtype, rows, D));
+  const size_t out_block = (size_t)(G * state_bytes(out_dtype, rows, D));
+  if (overlap(outs, in_block, out, out_block) || overlap(lses, (size_t)(P * rows) * 4, lse, (size_t)(G * rows) * 4) ||
+      overlap(outs, in_block, lse, (size_t)(G * rows) * 4) || overlap(lses, (size_t)(P * rows) * 4, out, out_block))
     return fail(AS_ERR_INVALID_ARG, "outputs overlap the input blocks");
-  if (overlap(out, (size_t)(G * rows * D) * eout, lse, (size_t)(G * rows) * 4))
-    return fail(AS_ERR_INVALID_ARG, "out and lse overlap");
+  if (overlap(out, out_block, lse, (size_t)(G * rows) * 4)) return fail(AS_ERR_INVALID_ARG, "out and lse overlap");
   as::MergeArgs a;
   memset(&a, 0, sizeof(a));
   a.base_out = outs; a.base_lse = lses; a.out = out; a.lse = lse;
   a.rows = rows; a.n = P; a.D = (int32_t)D; a.group = group;
-  a.in_bf16 = in_dtype == AS_BF16; a.out_bf16 = out_dtype == AS_BF16;
+  a.in_kind = out_kind(in_dtype); a.out_kind = out_kind(out_dtype);
+  a.payload_bytes = as::fp8_payload_bytes(rows, D);
   a.vec2 = D % 8 == 0;   // slices of rows*D elements keep 16-byte alignment when D % 8 == 0
   return hip_status(as::launch_merge(a, stream), "compose_groups launch");
 }
@@ -390,6 +428,11 @@ as_status as_merge(int32_t n, const float* const* outs, const float* const* lses
     for (int32_t i = 0; i < n; ++i) ptrs[i] = outs[i];
   return merge_impl(n, (n >= 1 && n <= AS_MAX_MERGE && outs) ? ptrs : nullptr, lses, AS_F32, rows, D, AS_F32, out, lse,
                     stream);
+}
+
+size_t as_state_bytes(as_dtype state_dtype, int64_t rows, int64_t D) {
+  if (out_kind(state_dtype) < 0 || rows < 0 || rows > kMaxRows || D < 1 || D > 1024) return 0;
+  return (size_t)state_bytes(state_dtype, rows, D);
 }
 
 size_t as_partition_contribution_workspace_size(int32_t P, int64_t rows, int64_t rows_per_group) {

@@ -9,6 +9,14 @@
 
 namespace as {
 
+// Storage of a state's OUT (the attention kernel's out_kind, the merge kernels' types).
+constexpr int kOutF32 = 0, kOutBF16 = 1, kOutFP8 = 2;
+
+// An fp8 state payload of `rows` rows of D: the E4M3 codes [rows][D], then one float32
+// factor per row at byte offset rows * D; a value is code * factor of its row. Payloads
+// of a block follow each other every payload_bytes (16-byte multiples).
+inline int64_t fp8_payload_bytes(int64_t rows, int64_t D) { return rows * D + (rows * 4 + 15) / 16 * 16; }
+
 // Arguments of one partition-attention launch, passed by value as the kernel
 // argument (the key ranges travel in the kernarg segment).
 struct AttnArgs {
@@ -17,16 +25,21 @@ struct AttnArgs {
   const void* v;
   int64_t q_sb, q_sh, q_ss;  // element strides of q over (b, h, s)
   int64_t k_sb, k_sh, k_ss;  // element strides of k and v over (b, h, s)
-  void* out;                 // [P][B][H][Sq][D], float or bf16 (out_bf16)
+  void* out;                 // [P][B][H][Sq][D] of out_kind (kOutFP8: P payloads)
   float* lse;                // [P][B][H][Sq]
   int32_t B, H, Sq, Skv, D, P;
   int32_t n_qtiles;          // ceil(Sq / rows per workgroup)
   float scale;               // softmax scale
   float scale_log2;          // scale * log2(e)
-  int32_t out_bf16;          // OUT stored as bf16 (rounded to nearest even) instead of float
-  int32_t qk_fp8;            // q and k are fp8 e4m3 (v stays bf16), dequantised by q_scale, k_scale
+  int32_t out_kind;          // OUT storage: kOutF32, kOutBF16 (rounded to nearest even) or
+                             // kOutFP8 (E4M3 codes with one factor per row: a state payload)
+  int32_t qk_fp8;            // q and k are fp8 e4m3, dequantised by q_scale, k_scale
+  int32_t v_fp8;             // v is fp8 e4m3 too, dequantised by v_scale (with qk_fp8 only)
   const float* q_scale;      // [B*H] (qk_fp8 only)
   const float* k_scale;      // [B*H] (qk_fp8 only)
+  const float* v_scale;      // [B*H] (v_fp8 only)
+  int64_t state_rows;        // B*H*Sq: rows of one partition's state
+  int64_t payload_bytes;     // kOutFP8: bytes of one partition's state payload
   int32_t ranges[2 * AS_MAX_PARTITIONS];
   // Grouped launches (as_partition_attn_grouped): `ranges` holds the non-empty
   // partitions only, packed in group order (P of them); group g holds packed partitions
@@ -49,17 +62,18 @@ hipError_t launch_fill_neg_inf(float* p, int64_t n, hipStream_t stream);
 // index k, whose inputs are slices k*group .. min((k+1)*group, P) - 1; outputs are
 // [G][rows][D] and [G][rows].
 struct MergeArgs {
-  const void* outs[AS_MAX_MERGE];   // float or bf16 [rows][D] each
+  const void* outs[AS_MAX_MERGE];   // [rows][D] of in_kind each (kOutFP8: a payload)
   const float* lses[AS_MAX_MERGE];
   const void* base_out;
   const float* base_lse;
-  void* out;                        // float or bf16
+  void* out;                        // [rows][D] of out_kind (kOutFP8: a payload)
   float* lse;
   int64_t rows;
   int32_t n;
   int32_t D;
   int32_t group;
-  int32_t in_bf16, out_bf16;
+  int32_t in_kind, out_kind;        // kOutF32, kOutBF16 or kOutFP8
+  int64_t payload_bytes;            // fp8 payload of `rows` rows (fp8_payload_bytes)
   int32_t vec2;   // bf16 inputs: every OUT pointer 16-byte aligned and D % 8 == 0 (16-byte lane loads)
 };
 
@@ -80,6 +94,8 @@ int attn_f32_rows_per_block(int D);
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream);   // bf16 or fp8 q/k (qk_fp8)
 hipError_t launch_attn_fp8(const AttnArgs& a, hipStream_t stream);    // fp8 q/k
+hipError_t launch_attn_fp8v(const AttnArgs& a, hipStream_t stream);   // fp8 q/k/v
+hipError_t launch_attn_grouped_fp8v(const AttnArgs& a, hipStream_t stream);   // grouped, fp8 q/k/v
 hipError_t launch_attn_grouped(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);

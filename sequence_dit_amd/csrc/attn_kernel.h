@@ -61,10 +61,11 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-// Stores of OUT elements: fp32, or bf16 rounded to nearest even.
-template <bool BF16>
+// Stores of OUT elements: fp32, or bf16 rounded to nearest even (fp8 payloads have their
+// own epilogue).
+template <int OUT>
 __device__ __forceinline__ void store_out4(void* base, int64_t off, f32x4 v) {
-  if (BF16) {
+  if (OUT == kOutBF16) {
     const bf16x4 h = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
     *reinterpret_cast<u32x2*>(static_cast<__bf16*>(base) + off) = __builtin_bit_cast(u32x2, h);
   } else {
@@ -72,11 +73,20 @@ __device__ __forceinline__ void store_out4(void* base, int64_t off, f32x4 v) {
   }
 }
 
-template <bool BF16>
+template <int OUT>
 __device__ __forceinline__ void store_out1(void* base, int64_t off, float v) {
-  if (BF16) static_cast<__bf16*>(base)[off] = (__bf16)v;
+  if (OUT == kOutBF16) static_cast<__bf16*>(base)[off] = (__bf16)v;
   else static_cast<float*>(base)[off] = v;
 }
+
+// Four values as E4M3 codes (one 32-bit word, lowest address first), rounded to nearest
+// even; callers keep |x| <= 448.
+__device__ __forceinline__ unsigned fp8x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (unsigned)w;
+}
+__device__ __forceinline__ float clamp448(float x) { return fminf(fmaxf(x, -448.0f), 448.0f); }
 
 constexpr int kWaves = 8;
 constexpr int kQB = 1;                       // 32-row query blocks per wave
@@ -451,8 +461,11 @@ struct TileCursor {
 // Tile staging. Group 1 (waves 4-7) owns K: 16-byte chunks, D / 8 (bf16) or D / 16
 // (fp8) lanes per row. Group 0 (waves 0-3) owns V: a unit is 4 keys x 8 d,
 // transposed in registers and written as 8-byte key groups of 8 V^T rows; KB / 4
-// consecutive lanes cover the key groups of one row.
-template <int D, bool QK8>
+// consecutive lanes cover the key groups of one row. fp8 V (V8): a unit's 4 keys
+// arrive as 8-byte loads of 8 E4M3 codes and are widened to bf16 (exact: every E4M3
+// value is a bf16 value) before the same transposition, so LDS and the PV MFMA see
+// bf16 V^T and the per-(b, h) factor of V is applied to OUT in the epilogue.
+template <int D, bool QK8, bool V8 = false>
 struct Stager {
   static constexpr int KCH = QK8 ? D / 16 : D / 8;  // 16-byte chunks per K row
   static constexpr int VCH = D / 8;                 // 16-byte chunks per V row
@@ -463,6 +476,7 @@ struct Stager {
   static constexpr int VUNITS = (KB / 4) * VCH;     // V units per tile
   static constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw 32-bit buffer, no swizzle
   u32x4 r[4];
+  u32x2 r8[4];           // fp8 V: the 8 codes of each of the unit's 4 keys
   const char* src;       // K or V rows of this (b, h): from the partition's first key, or
                          // (grouped launches) from key 0
   int stride_bytes;      // between rows
@@ -512,8 +526,18 @@ struct Stager {
   __device__ __forceinline__ void load_k(int tile) { load_k_from(tile_rsrc(tile)); }
   __device__ __forceinline__ void load_v_from(__amdgpu_buffer_rsrc_t rs) {
     if (!on) return;
+    if constexpr (V8) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) r[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff[j], 0, 0);
+      for (int j = 0; j < 4; ++j) r8[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, voff[j], 0, 0));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff[j], 0, 0);
+    }
+  }
+  // 2 E4M3 codes (bytes 0-1, or 2-3 for HI, of x) as a bf16 pair, exactly
+  template <bool HI>
+  __device__ __forceinline__ static unsigned widen2(unsigned x) {
+    return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, HI));
   }
   template <int SLOT>
   __device__ __forceinline__ void store_k(char* smem) {
@@ -530,6 +554,11 @@ struct Stager {
   __device__ __forceinline__ void store_v(char* smem) {
     using L = Lds<D, QK8>;
     if (!on) return;
+    if constexpr (V8) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        r[j] = u32x4{widen2<false>(r8[j][0]), widen2<true>(r8[j][0]), widen2<false>(r8[j][1]), widen2<true>(r8[j][1])};
+    }
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const unsigned v0 = r[0][w], v1 = r[1][w], v2 = r[2][w], v3 = r[3][w];
@@ -560,14 +589,19 @@ struct Stager {
 // groups). Each partition's LSE comes from a row sum restarted at the partition; the
 // group's composed state is written once, optionally composed with a given state (a
 // cached one) in the epilogue.
-template <int D, bool OUT_BF16, bool QK8, bool GROUPED = false>
+//
+// OUT: kOutF32, kOutBF16, or kOutFP8: a state payload (E4M3 codes of OUT / f with one
+// factor f = max|OUT| / 448 per row; single-partition launches only). V8: fp8 V (with
+// QK8).
+template <int D, int OUT, bool QK8, bool GROUPED = false, bool V8 = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_kernel(const AttnArgs a) {
   using L = Lds<D, QK8>;
   using W = Wave<D, QK8, GROUPED>;
-  using St = Stager<D, QK8>;
+  using St = Stager<D, QK8, V8>;
   static_assert(kQB == 1 && St::KLOADS >= 1 && St::KLOADS <= 4 && St::VUNITS <= St::GT, "tile shape");
-  static_assert(!(GROUPED && OUT_BF16), "grouped launches write fp32 states");
+  static_assert(!(GROUPED && OUT != kOutF32), "grouped launches write fp32 states");
+  static_assert(!V8 || QK8, "fp8 V comes with fp8 Q and K");
   __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
   // grouped launches: (first key, keys, caller's index) of every partition of the group
   __shared__ int gtab[GROUPED ? 3 * AS_MAX_PARTITIONS : 1];
@@ -612,7 +646,14 @@ void attn_bf16_kernel(const AttnArgs a) {
         const int q = q0 + r;
         if (q < a.Sq) {
           lse[q] = -INFINITY;
-          for (int c = 0; c < D / 4; ++c) store_out4<OUT_BF16>(a.out, (row_base + q) * D + 4 * c, f32x4{0.f, 0.f, 0.f, 0.f});
+          if constexpr (OUT == kOutFP8) {   // codes 0, factor 0
+            char* pay = static_cast<char*>(a.out) + (int64_t)part * a.payload_bytes;
+            const int64_t srow = (int64_t)bh * a.Sq + q;
+            for (int c = 0; c < D / 16; ++c) *reinterpret_cast<u32x4*>(pay + srow * D + 16 * c) = u32x4{0u, 0u, 0u, 0u};
+            reinterpret_cast<float*>(pay + a.state_rows * D)[srow] = 0.f;
+          } else {
+            for (int c = 0; c < D / 4; ++c) store_out4<OUT>(a.out, (row_base + q) * D + 4 * c, f32x4{0.f, 0.f, 0.f, 0.f});
+          }
         }
       }
       return;
@@ -677,12 +718,13 @@ void attn_bf16_kernel(const AttnArgs a) {
     st.w_off = row * L::KP + ch * 16;
     st.on = true;
   } else {
-    st.stride_bytes = (int)(a.k_ss * 2);
-    st.row_bytes = D * 2;
-    kv_base = reinterpret_cast<const char*>(a.v) + kv_bh * 2;
+    constexpr int ev = V8 ? 1 : 2;    // bytes per V element
+    st.stride_bytes = (int)(a.k_ss * ev);
+    st.row_bytes = D * ev;
+    kv_base = reinterpret_cast<const char*>(a.v) + kv_bh * ev;
     const int va = gtid % (KB / 4), vc = gtid / (KB / 4);   // 4-key group, 8-wide d chunk
 #pragma unroll
-    for (int j = 0; j < 4; ++j) st.voff[j] = (4 * va + j) * st.stride_bytes + vc * 16;
+    for (int j = 0; j < 4; ++j) st.voff[j] = (4 * va + j) * st.stride_bytes + vc * 8 * ev;
     st.w_off = L::V0 + (8 * vc) * L::VP + vt_group_pos(va);
     st.on = gtid < St::VUNITS;
   }
@@ -848,7 +890,8 @@ void attn_bf16_kernel(const AttnArgs a) {
     // ---- epilogue: the group's composed state, composed with the given state for group 0
     const float lt = wave_sum_halves(w.l);
     if (qrow < a.Sq) {
-      float wo = lt > 0.f ? 1.0f / lt : 0.f;   // weight of O
+      // weight of O (fp8 V: O is in units of V's factor)
+      float wo = lt > 0.f ? (V8 ? a.v_scale[bh] : 1.0f) / lt : 0.f;
       float L = lt > 0.f ? (w.m + __log2f(lt)) * 0.69314718055994530942f : -INFINITY;
       float wc = 0.f;                          // weight of the given state's OUT
       const bool fold = a.fold_out != nullptr && part == 0;
@@ -878,7 +921,7 @@ void attn_bf16_kernel(const AttnArgs a) {
             val = f32x4{__builtin_fmaf(wc, c[0], val[0]), __builtin_fmaf(wc, c[1], val[1]),
                         __builtin_fmaf(wc, c[2], val[2]), __builtin_fmaf(wc, c[3], val[3])};
           }
-          store_out4<false>(a.out, orow + d, val);
+          store_out4<kOutF32>(a.out, orow + d, val);
         }
       if (half == 0) lse[qrow] = L;
     }
@@ -891,8 +934,37 @@ void attn_bf16_kernel(const AttnArgs a) {
 
     // ---- epilogue: OUT = O / l, LSE = (m + log2 l) ln 2
     const float lt = wave_sum_halves(w.l);
-    const float inv = 1.0f / lt;
-    if (qrow < a.Sq) {
+    const float inv = (V8 ? a.v_scale[bh] : 1.0f) / lt;   // fp8 V: O is in units of V's factor
+    if constexpr (OUT == kOutFP8) {
+      // The row's largest |OUT| (the two halves of a row hold its two halves of D); OUT
+      // is stored as the E4M3 codes of OUT * (448 / amax), rounded to nearest even, with
+      // the factor amax / 448 (0 for a zero row, whose codes are 0).
+      float mx = 0.f;
+#pragma unroll
+      for (int db = 0; db < W::NDB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(w.o[db][e]));
+      const float amax = wave_max_halves(mx) * fabsf(inv);   // = max |O * inv|: rounding is monotone
+      const float qf = amax > 0.f ? 448.0f / amax : 0.f;
+      if (qrow < a.Sq) {
+        char* pay = static_cast<char*>(a.out) + (int64_t)part * a.payload_bytes;
+        const int64_t srow = (int64_t)bh * a.Sq + qrow;
+        unsigned char* crow = reinterpret_cast<unsigned char*>(pay) + srow * D;
+#pragma unroll
+        for (int db = 0; db < W::NDB; ++db)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = clamp448((w.o[db][4 * j + e] * inv) * qf);
+            *reinterpret_cast<unsigned*>(crow + db * 32 + 8 * j + 4 * half) = fp8x4(x[0], x[1], x[2], x[3]);
+          }
+        if (half == 0) {
+          reinterpret_cast<float*>(pay + a.state_rows * D)[srow] = amax / 448.0f;
+          lse[qrow] = (w.m + __log2f(lt)) * 0.69314718055994530942f;
+        }
+      }
+    } else if (qrow < a.Sq) {
       const int64_t orow = (row_base + qrow) * D;
 #pragma unroll
       for (int db = 0; db < W::NDB; ++db)
@@ -900,11 +972,49 @@ void attn_bf16_kernel(const AttnArgs a) {
         for (int j = 0; j < 4; ++j) {
           const f32x4 val = {w.o[db][4 * j] * inv, w.o[db][4 * j + 1] * inv, w.o[db][4 * j + 2] * inv,
                              w.o[db][4 * j + 3] * inv};
-          store_out4<OUT_BF16>(a.out, orow + db * 32 + 8 * j + 4 * half, val);
+          store_out4<OUT>(a.out, orow + db * 32 + 8 * j + 4 * half, val);
         }
       if (half == 0) lse[qrow] = (w.m + __log2f(lt)) * 0.69314718055994530942f;
     }
   }
+}
+
+// Launch of one instance: D from the arguments, OUT from a.out_kind (single-partition
+// launches; grouped ones write fp32 states).
+template <int D, int OUT, bool QK8, bool GROUPED, bool V8>
+hipError_t launch_instance(const AttnArgs& a, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL((attn_bf16_kernel<D, OUT, QK8, GROUPED, V8>), grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D, bool QK8, bool GROUPED, bool V8>
+hipError_t launch_for_d(const AttnArgs& a, dim3 grid, hipStream_t stream) {
+  if constexpr (GROUPED) {
+    return launch_instance<D, kOutF32, QK8, true, V8>(a, grid, stream);
+  } else {
+    switch (a.out_kind) {
+      case kOutF32: return launch_instance<D, kOutF32, QK8, false, V8>(a, grid, stream);
+      case kOutBF16: return launch_instance<D, kOutBF16, QK8, false, V8>(a, grid, stream);
+      case kOutFP8: return launch_instance<D, kOutFP8, QK8, false, V8>(a, grid, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+}
+
+template <bool QK8, bool GROUPED, bool V8>
+hipError_t launch_variant(const AttnArgs& a, dim3 grid, hipStream_t stream) {
+  if (a.D == 128) return launch_for_d<128, QK8, GROUPED, V8>(a, grid, stream);
+  if (a.D == 64) return launch_for_d<64, QK8, GROUPED, V8>(a, grid, stream);
+  return hipErrorInvalidValue;
+}
+
+// Grid of a single-partition launch (query tiles x B*H x P), or of a grouped one: units
+// (group, b, h) padded to a multiple of 8 (the kernel's XCD mapping), times query tiles.
+// Zero blocks: nothing to launch; -1: too many.
+inline int64_t attn_grid(const AttnArgs& a, bool grouped) {
+  const int64_t total = grouped ? ((int64_t)a.G * a.B * a.H + 7) / 8 * 8 * a.n_qtiles
+                                : (int64_t)a.n_qtiles * a.B * a.H * a.P;
+  return total > 0x7fffffff ? -1 : total;
 }
 
 }  // namespace

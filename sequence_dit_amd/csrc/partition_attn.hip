@@ -105,36 +105,27 @@ int attn_f32_rows_per_block(int) { return kF32Rows; }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream) {
   if (a.qk_fp8) return launch_attn_fp8(a, stream);
-  const int64_t total = (int64_t)a.n_qtiles * a.B * a.H * a.P;
-  if (total <= 0) return hipSuccess;
-  if (total > 0x7fffffff) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)total), block(kThreads);
-  if (a.D == 128) {
-    if (a.out_bf16) hipLaunchKernelGGL((attn_bf16_kernel<128, true, false>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<128, false, false>), grid, block, 0, stream, a);
-  } else if (a.D == 64) {
-    if (a.out_bf16) hipLaunchKernelGGL((attn_bf16_kernel<64, true, false>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<64, false, false>), grid, block, 0, stream, a);
-  } else {
-    return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  const int64_t total = attn_grid(a, false);
+  if (total == 0) return hipSuccess;
+  if (total < 0) return hipErrorInvalidConfiguration;
+  return launch_variant<false, false, false>(a, dim3((unsigned)total), stream);
 }
 
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream) {
+  if (a.out_kind != kOutF32 && a.out_kind != kOutBF16) return hipErrorInvalidValue;
   const int64_t gy = (int64_t)a.B * a.H * a.P;
   if (gy <= 0 || a.Sq <= 0) return hipSuccess;
   if (gy > 65535) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)((a.Sq + kF32Rows - 1) / kF32Rows), (unsigned)gy), block(kF32Threads);
   const int dc = a.D / 4;
   if (dc <= 8) {
-    if (a.out_bf16) hipLaunchKernelGGL((attn_f32_kernel<8, true>), grid, block, 0, stream, a);
+    if (a.out_kind == kOutBF16) hipLaunchKernelGGL((attn_f32_kernel<8, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((attn_f32_kernel<8, false>), grid, block, 0, stream, a);
   } else if (dc <= 16) {
-    if (a.out_bf16) hipLaunchKernelGGL((attn_f32_kernel<16, true>), grid, block, 0, stream, a);
+    if (a.out_kind == kOutBF16) hipLaunchKernelGGL((attn_f32_kernel<16, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((attn_f32_kernel<16, false>), grid, block, 0, stream, a);
   } else if (dc <= 32) {
-    if (a.out_bf16) hipLaunchKernelGGL((attn_f32_kernel<32, true>), grid, block, 0, stream, a);
+    if (a.out_kind == kOutBF16) hipLaunchKernelGGL((attn_f32_kernel<32, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((attn_f32_kernel<32, false>), grid, block, 0, stream, a);
   } else {
     return hipErrorInvalidValue;

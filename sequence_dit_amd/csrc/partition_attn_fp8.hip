@@ -7,20 +7,11 @@
 namespace as {
 
 hipError_t launch_attn_fp8(const AttnArgs& a, hipStream_t stream) {
-  const int64_t total = (int64_t)a.n_qtiles * a.B * a.H * a.P;
-  if (total <= 0) return hipSuccess;
-  if (total > 0x7fffffff) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)total), block(kThreads);
-  if (a.D == 128) {
-    if (a.out_bf16) hipLaunchKernelGGL((attn_bf16_kernel<128, true, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<128, false, true>), grid, block, 0, stream, a);
-  } else if (a.D == 64) {
-    if (a.out_bf16) hipLaunchKernelGGL((attn_bf16_kernel<64, true, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<64, false, true>), grid, block, 0, stream, a);
-  } else {
-    return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  if (a.v_fp8) return launch_attn_fp8v(a, stream);
+  const int64_t total = attn_grid(a, false);
+  if (total == 0) return hipSuccess;
+  if (total < 0) return hipErrorInvalidConfiguration;
+  return launch_variant<true, false, false>(a, dim3((unsigned)total), stream);
 }
 
 }  // namespace as

@@ -26,22 +26,12 @@ hipError_t launch_fill_neg_inf(float* p, int64_t n, hipStream_t stream) {
 }
 
 hipError_t launch_attn_grouped(const AttnArgs& a, hipStream_t stream) {
-  // units (group, b, h) padded to a multiple of 8: see the kernel's XCD mapping
-  const int64_t units = (int64_t)a.G * a.B * a.H;
-  const int64_t total = (units + 7) / 8 * 8 * a.n_qtiles;
-  if (total <= 0) return hipSuccess;
-  if (total > 0x7fffffff) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)total), block(kThreads);
-  if (a.qk_fp8) {
-    if (a.D == 128) hipLaunchKernelGGL((attn_bf16_kernel<128, false, true, true>), grid, block, 0, stream, a);
-    else if (a.D == 64) hipLaunchKernelGGL((attn_bf16_kernel<64, false, true, true>), grid, block, 0, stream, a);
-    else return hipErrorInvalidValue;
-  } else {
-    if (a.D == 128) hipLaunchKernelGGL((attn_bf16_kernel<128, false, false, true>), grid, block, 0, stream, a);
-    else if (a.D == 64) hipLaunchKernelGGL((attn_bf16_kernel<64, false, false, true>), grid, block, 0, stream, a);
-    else return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  if (a.v_fp8) return launch_attn_grouped_fp8v(a, stream);
+  const int64_t total = attn_grid(a, true);
+  if (total == 0) return hipSuccess;
+  if (total < 0) return hipErrorInvalidConfiguration;
+  if (a.qk_fp8) return launch_variant<true, true, false>(a, dim3((unsigned)total), stream);
+  return launch_variant<false, true, false>(a, dim3((unsigned)total), stream);
 }
 
 }  // namespace as

@@ -257,13 +257,44 @@ def quantize_fp8(x: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
 
 def small_case_fp8(seed: int, B: int, H: int, Sq: int, Skv: int, D: int, ranges: Sequence[Range],
                    std: float = 1.0) -> Workload:
-    """small_case with fp8 queries and keys: w.q8, w.k8 (float8_e4m3fn codes) and
-    w.q_scale, w.k_scale (float32 [B, H]) are attached; v stays bf16."""
+    """small_case with fp8 codes attached: w.q8, w.k8, w.v8 (float8_e4m3fn) with their
+    factors w.q_scale, w.k_scale, w.v_scale (float32 [B, H]); w.v stays the bf16 values
+    (the fp8-q/k path takes those)."""
     w = small_case(seed, B, H, Sq, Skv, D, ranges, torch.bfloat16, std)
     w.q8, w.q_scale = quantize_fp8(w.q)
     w.k8, w.k_scale = quantize_fp8(w.k)
+    w.v8, w.v_scale = quantize_fp8(w.v)
     w.name = f"fp8 {w.name}"
     return w
+
+
+def with_fp8(w: Workload) -> Workload:
+    """A workload with per-(b, h) fp8 codes of its q, k and v attached (as small_case_fp8)."""
+    w.q8, w.q_scale = quantize_fp8(w.q)
+    w.k8, w.k_scale = quantize_fp8(w.k)
+    w.v8, w.v_scale = quantize_fp8(w.v)
+    return w
+
+
+TENSOR_FP8_STATE = 8
+
+
+def random_fp8_states(seed: int, n: int, rows: int, D: int, n_empty: int = 0):
+    """n fp8 state payload contents of rows x D, for composition tests: codes (uint8 [n, rows, D])
+    drawn uniformly over the finite E4M3 codes (a NaN code is replaced by 0x7E), row factors
+    (float32 [n, rows]) exp(N(0, 1)) / 256, LSE (float32 [n, rows]) 4 N(0, 1); n_empty random
+    (state, row) pairs are empty states: codes 0, factor 0, LSE -inf."""
+    g = np.random.default_rng([2000 + seed, TENSOR_FP8_STATE])
+    codes = g.integers(0, 256, size=(n, rows, D), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x7E
+    factors = (np.exp(g.standard_normal((n, rows))) / 256).astype(np.float32)
+    lses = (g.standard_normal((n, rows)) * 4).astype(np.float32)
+    if n_empty:
+        idx = g.choice(n * rows, size=n_empty, replace=False)
+        codes.reshape(n * rows, D)[idx] = 0
+        factors.reshape(-1)[idx] = 0
+        lses.reshape(-1)[idx] = -np.inf
+    return codes, factors, lses
 
 
 WORKLOADS = {1: tiny_fp32, 2: image_dit, 3: video_dit, 4: long_video, 5: selective_reuse}

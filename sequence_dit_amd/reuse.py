@@ -21,6 +21,15 @@ import torch
 from . import _native
 
 
+def _v_scale(v: torch.Tensor, scales):
+    """V's factors when v holds fp8 codes (scales = (q_scale, k_scale, v_scale)), else None."""
+    if v.dtype != torch.float8_e4m3fn:
+        return None
+    if scales is None or len(scales) < 3:
+        raise ValueError("fp8 v needs its dequantisation factors (scales = (q_scale, k_scale, v_scale))")
+    return scales[2]
+
+
 class SelectiveReuse:
     """Preallocated buffers and call order for one query shard against P partitions."""
 
@@ -85,18 +94,23 @@ class SelectiveReuse:
         return r
 
     def _attn(self, name: str, q, k, v, ranges, out, lse, scales) -> None:
-        """Partition states: bf16 (or fp32) q/k/v, or fp8 E4M3 q/k with scales = (q_scale, k_scale)."""
+        """Partition states: bf16 (or fp32) q/k/v, or fp8 E4M3 q/k with scales = (q_scale, k_scale),
+        or fp8 q/k/v with scales = (q_scale, k_scale, v_scale)."""
         if q.dtype == torch.float8_e4m3fn:
             if scales is None:
                 raise ValueError("fp8 q/k need their dequantisation factors (q_scale, k_scale)")
-            self._timed(name, _native.partition_attn_fp8, q, k, v, scales[0], scales[1], ranges, self.scale,
-                        out=out, lse=lse)
+            if v.dtype == torch.float8_e4m3fn:
+                self._timed(name, _native.partition_attn_fp8_qkv, q, k, v, scales[0], scales[1], scales[2], ranges,
+                            self.scale, out=out, lse=lse)
+            else:
+                self._timed(name, _native.partition_attn_fp8, q, k, v, scales[0], scales[1], ranges, self.scale,
+                            out=out, lse=lse)
         else:
             self._timed(name, _native.partition_attn, q, k, v, ranges, self.scale, out=out, lse=lse)
 
     def anchor(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scales=None) -> None:
         """Step t: all partition states, their weights, and the cached composition of the far ones.
-        q and k may be fp8 E4M3 codes, with scales = (q_scale, k_scale) float32 [B, H]."""
+        q and k (and v) may be fp8 E4M3 codes, with scales = (q_scale, k_scale[, v_scale]) float32 [B, H]."""
         self._attn("attn_anchor", q, k, v, self.ranges, self.state_out, self.state_lse, scales)
         self._timed("contrib_anchor", self._contribution, self.state_lse, self.anchor_weights, self.anchor_scores)
         self._timed("merge_cached", _native.merge, [self.state_out[i] for i in self.far],
@@ -143,7 +157,7 @@ class SelectiveReuse:
         fp8 = scales is not None
         self._timed("attn_anchor_grouped", _native.partition_attn_grouped, q, k, v, [self.ranges[i] for i in order],
                     starts, self.scale, None, True, scales[0] if fp8 else None, scales[1] if fp8 else None,
-                    self.group_out, self.group_lse, self.state_lse)
+                    self.group_out, self.group_lse, self.state_lse, v_scale=_v_scale(v, scales))
         self._timed("contrib_anchor", self._contribution, self.state_lse, self.anchor_weights, self.anchor_scores)
         self._timed("merge_cached_grouped", _native.merge, [self.group_out[g] for g in range(n_far_groups)],
                     [self.group_lse[g] for g in range(n_far_groups)], out=self.cached_out, lse=self.cached_lse)
@@ -168,7 +182,8 @@ class SelectiveReuse:
                                                                                           self.step_group_lse)
         self._timed("attn_fresh_grouped", _native.partition_attn_grouped, q, k, v,
                     [self.ranges[i] for i in self.near], starts, self.scale, (self.cached_out, self.cached_lse), True,
-                    scales[0] if fp8 else None, scales[1] if fp8 else None, dst_out, dst_lse, self.step_lse[:nf])
+                    scales[0] if fp8 else None, scales[1] if fp8 else None, dst_out, dst_lse, self.step_lse[:nf],
+                    v_scale=_v_scale(v, scales))
         if G > 1:
             self._timed("merge_step_grouped", _native.merge, list(self.step_group_out), list(self.step_group_lse),
                         out=self.result_out, lse=self.result_lse)

@@ -50,23 +50,43 @@ void attn_calls() {
   CHECK(strcmp(stub::last.kind, "attn_bf16") == 0);
   const as::AttnArgs& a = stub::last.attn;
   CHECK(a.B == B && a.H == H && a.Sq == Sq && a.Skv == Skv && a.D == D && a.P == P && a.n_qtiles == 2);
-  CHECK(a.q_ss == D && a.k_sh == Skv * D && a.out == out && a.lse == lse && a.out_bf16 == 0 && a.qk_fp8 == 0);
+  CHECK(a.q_ss == D && a.k_sh == Skv * D && a.out == out && a.lse == lse && a.out_kind == 0 && a.qk_fp8 == 0);
   for (int i = 0; i < 2 * P; ++i) CHECK(a.ranges[i] == flat[i]);
   CHECK(fabsf(a.scale_log2 - 0.088f * 1.44269504f) < 1e-6f);
 
   // compact states, fp8 q/k, f32 path
   CHECK(as_partition_attn_states(q, k, v, AS_BF16, B, H, Sq, Skv, D, qs, ks, r.get(), P, 0.f, AS_BF16, out,
                                  (float*)lse, nullptr) == AS_OK);
-  CHECK(stub::last.attn.out_bf16 == 1 && stub::last.attn.scale_log2 == 0.f);
+  CHECK(stub::last.attn.out_kind == 1 && stub::last.attn.scale_log2 == 0.f);
   float* qsc = (float*)fake(0x60000000);
   float* ksc = (float*)fake(0x60001000);
   CHECK(as_partition_attn_fp8(q, k, v, qsc, ksc, B, H, Sq, Skv, D, qs, ks, r.get(), P, 0.088f, AS_F32, out,
                               (float*)lse, nullptr) == AS_OK);
   CHECK(stub::last.attn.qk_fp8 == 1 && stub::last.attn.q_scale == qsc && stub::last.attn.k_scale == ksc);
+  CHECK(stub::last.attn.v_fp8 == 0);
+  // fp8 state payloads: P payloads of B*H*Sq rows, factors after the codes
+  const int64_t rows = B * H * Sq;
+  CHECK(as_state_bytes(AS_FP8_E4M3, rows, D) == (size_t)(rows * D + (4 * rows + 15) / 16 * 16));
+  CHECK(as_state_bytes(AS_BF16, rows, D) == (size_t)(rows * D * 2) && as_state_bytes((as_dtype)7, rows, D) == 0);
+  CHECK(as_partition_attn_states(q, k, v, AS_BF16, B, H, Sq, Skv, D, qs, ks, r.get(), P, 0.1f, AS_FP8_E4M3, out,
+                                 (float*)lse, nullptr) == AS_OK);
+  CHECK(stub::last.attn.out_kind == 2 && stub::last.attn.state_rows == rows &&
+        stub::last.attn.payload_bytes == (int64_t)as_state_bytes(AS_FP8_E4M3, rows, D));
+  // fp8 q/k/v: v's factors; an output over them is refused; f32 inputs cannot write fp8 states
+  float* vsc = (float*)fake(0x60002000);
+  CHECK(as_partition_attn_fp8_qkv(q, k, v, qsc, ksc, vsc, B, H, Sq, Skv, D, qs, ks, r.get(), P, 0.088f,
+                                  AS_FP8_E4M3, out, (float*)lse, nullptr) == AS_OK);
+  CHECK(stub::last.attn.v_fp8 == 1 && stub::last.attn.v_scale == vsc && stub::last.attn.out_kind == 2);
+  CHECK(as_partition_attn_fp8_qkv(q, k, v, qsc, ksc, nullptr, B, H, Sq, Skv, D, qs, ks, r.get(), P, 0.088f, AS_F32,
+                                  out, (float*)lse, nullptr) == AS_ERR_INVALID_ARG);
+  CHECK(as_partition_attn_fp8_qkv(q, k, v, qsc, ksc, vsc, B, H, Sq, Skv, D, qs, ks, r.get(), P, 0.088f, AS_F32,
+                                  vsc - 4, (float*)lse, nullptr) == AS_ERR_INVALID_ARG);
   const int64_t qs40[3] = {H * Sq * 40, Sq * 40, 40}, ks40[3] = {H * Skv * 40, Skv * 40, 40};
   CHECK(as_partition_attn(q, k, v, AS_F32, B, H, Sq, Skv, 40, qs40, ks40, r.get(), P, 0.15f, (float*)out,
                           (float*)lse, nullptr) == AS_OK);
   CHECK(strcmp(stub::last.kind, "attn_f32") == 0 && stub::last.attn.n_qtiles == 5);
+  CHECK(as_partition_attn_states(q, k, v, AS_F32, B, H, Sq, Skv, 40, qs40, ks40, r.get(), P, 0.15f, AS_FP8_E4M3, out,
+                                 (float*)lse, nullptr) == AS_ERR_UNSUPPORTED);
 
   // grouped: the empty partition (2 of the 7) is packed out, its LSE filled with -inf
   {
@@ -74,7 +94,7 @@ void attn_calls() {
     auto starts = ranges(gs);
     float* part = (float*)fake(0x70000000);
     stub::fills.clear();
-    CHECK(as_partition_attn_grouped(q, k, v, AS_BF16, nullptr, nullptr, B, H, Sq, Skv, D, qs, ks, r.get(), P,
+    CHECK(as_partition_attn_grouped(q, k, v, AS_BF16, nullptr, nullptr, nullptr, B, H, Sq, Skv, D, qs, ks, r.get(), P,
                                     starts.get(), 3, 0.088f, nullptr, nullptr, (float*)out, (float*)lse, part,
                                     nullptr) == AS_OK);
     const as::AttnArgs& g = stub::last.attn;
@@ -89,26 +109,26 @@ void attn_calls() {
     // group_starts not running from 0 to P, decreasing, G out of range, half a fold
     const std::vector<int32_t> bad1 = {0, 3, 6}, bad2 = {0, 4, 3, 7}, bad3 = {1, 7};
     auto b1 = ranges(bad1), b2 = ranges(bad2), b3 = ranges(bad3);
-    CHECK(as_partition_attn_grouped(q, k, v, AS_BF16, nullptr, nullptr, B, H, Sq, Skv, D, qs, ks, r.get(), P,
+    CHECK(as_partition_attn_grouped(q, k, v, AS_BF16, nullptr, nullptr, nullptr, B, H, Sq, Skv, D, qs, ks, r.get(), P,
                                     b1.get(), 2, 0.1f, nullptr, nullptr, (float*)out, (float*)lse, part,
                                     nullptr) == AS_ERR_INVALID_ARG);
-    CHECK(as_partition_attn_grouped(q, k, v, AS_BF16, nullptr, nullptr, B, H, Sq, Skv, D, qs, ks, r.get(), P,
+    CHECK(as_partition_attn_grouped(q, k, v, AS_BF16, nullptr, nullptr, nullptr, B, H, Sq, Skv, D, qs, ks, r.get(), P,
                                     b2.get(), 3, 0.1f, nullptr, nullptr, (float*)out, (float*)lse, part,
                                     nullptr) == AS_ERR_INVALID_ARG);
-    CHECK(as_partition_attn_grouped(q, k, v, AS_BF16, nullptr, nullptr, B, H, Sq, Skv, D, qs, ks, r.get(), P,
+    CHECK(as_partition_attn_grouped(q, k, v, AS_BF16, nullptr, nullptr, nullptr, B, H, Sq, Skv, D, qs, ks, r.get(), P,
                                     b3.get(), 1, 0.1f, nullptr, nullptr, (float*)out, (float*)lse, part,
                                     nullptr) == AS_ERR_INVALID_ARG);
-    CHECK(as_partition_attn_grouped(q, k, v, AS_BF16, nullptr, nullptr, B, H, Sq, Skv, D, qs, ks, r.get(), P,
+    CHECK(as_partition_attn_grouped(q, k, v, AS_BF16, nullptr, nullptr, nullptr, B, H, Sq, Skv, D, qs, ks, r.get(), P,
                                     starts.get(), 0, 0.1f, nullptr, nullptr, (float*)out, (float*)lse, part,
                                     nullptr) == AS_ERR_INVALID_ARG);
-    CHECK(as_partition_attn_grouped(q, k, v, AS_BF16, nullptr, nullptr, B, H, Sq, Skv, D, qs, ks, r.get(), P,
+    CHECK(as_partition_attn_grouped(q, k, v, AS_BF16, nullptr, nullptr, nullptr, B, H, Sq, Skv, D, qs, ks, r.get(), P,
                                     starts.get(), 3, 0.1f, (const float*)fake(0x60000000), nullptr, (float*)out,
                                     (float*)lse, part, nullptr) == AS_ERR_INVALID_ARG);
-    CHECK(as_partition_attn_grouped(q, k, v, AS_F32, nullptr, nullptr, B, H, Sq, Skv, D, qs, ks, r.get(), P,
+    CHECK(as_partition_attn_grouped(q, k, v, AS_F32, nullptr, nullptr, nullptr, B, H, Sq, Skv, D, qs, ks, r.get(), P,
                                     starts.get(), 3, 0.1f, nullptr, nullptr, (float*)out, (float*)lse, part,
                                     nullptr) == AS_ERR_INVALID_ARG);
     // the fold state overlapping an output
-    CHECK(as_partition_attn_grouped(q, k, v, AS_BF16, nullptr, nullptr, B, H, Sq, Skv, D, qs, ks, r.get(), P,
+    CHECK(as_partition_attn_grouped(q, k, v, AS_BF16, nullptr, nullptr, nullptr, B, H, Sq, Skv, D, qs, ks, r.get(), P,
                                     starts.get(), 3, 0.1f, (const float*)out, (const float*)fake(0x61000000),
                                     (float*)out, (float*)lse, part, nullptr) == AS_ERR_INVALID_ARG);
   }
@@ -157,7 +177,11 @@ void merge_calls() {
     for (int i = 0; i < n; ++i) vouts[i] = outs[i];
     CHECK(as_merge_states(n, vouts.get(), lses.get(), AS_BF16, rows, D, AS_F32, fake(0x90000000),
                           (float*)fake(0xa0000000), nullptr) == AS_OK);
-    CHECK(stub::last.merge.in_bf16 == 1 && stub::last.merge.out_bf16 == 0);
+    CHECK(stub::last.merge.in_kind == 1 && stub::last.merge.out_kind == 0);
+    CHECK(as_merge_states(n, vouts.get(), lses.get(), AS_FP8_E4M3, rows, D, AS_FP8_E4M3, fake(0x90000000),
+                          (float*)fake(0xa0000000), nullptr) == AS_OK);
+    CHECK(stub::last.merge.in_kind == 2 && stub::last.merge.out_kind == 2 &&
+          stub::last.merge.payload_bytes == (int64_t)as_state_bytes(AS_FP8_E4M3, rows, D));
     // n one beyond the list: refused before reading it
     CHECK(as_merge(n + AS_MAX_MERGE, outs.get(), lses.get(), rows, D, (float*)fake(0x90000000),
                    (float*)fake(0xa0000000), nullptr) == AS_ERR_INVALID_ARG);
@@ -172,6 +196,12 @@ void merge_calls() {
   CHECK(as_compose_groups(fake(0x10000000), (const float*)fake(0x80000000), AS_BF16, 32, rows, D, 4, AS_BF16,
                           fake(0x90000000), (float*)fake(0xa0000000), nullptr) == AS_OK);
   CHECK(stub::last.merge.group == 4 && stub::last.merge.n == 32);
+  CHECK(as_compose_groups(fake(0x10000000), (const float*)fake(0x80000000), AS_FP8_E4M3, 32, rows, D, 4, AS_F32,
+                          fake(0x90000000), (float*)fake(0xa0000000), nullptr) == AS_OK);
+  CHECK(stub::last.merge.in_kind == 2 && stub::last.merge.out_kind == 0);
+  // fp8 states need D in {32, 64, 128, 256}
+  CHECK(as_compose_groups(fake(0x10000000), (const float*)fake(0x80000000), AS_FP8_E4M3, 32, rows, 96, 4, AS_F32,
+                          fake(0x90000000), (float*)fake(0xa0000000), nullptr) == AS_ERR_UNSUPPORTED);
   CHECK(as_compose_groups(fake(0x10000000), (const float*)fake(0x80000000), AS_BF16, 32, INT64_MAX / 2, D, 4,
                           AS_BF16, fake(0x90000000), (float*)fake(0xa0000000), nullptr) == AS_ERR_UNSUPPORTED);
 }

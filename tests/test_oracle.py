@@ -402,6 +402,13 @@ def check_fp8(orc):
             for i in range(4):
                 for j in range(5):
                     assert got[b, h, i, j] == FP8_ALL[int(cq[b, h, i, j])] * sc[b, h]
+    # fp8 states: one factor per row (rows != D, so a factor taken per column fails)
+    fr = np.array([[0.5, 3.0, 0.0, 7.0], [2.0, 0.25, 1.0, 5.0]])
+    st = orc.fp8.decode_state(cq[0, :2], fr)
+    for s_ in range(2):
+        for r in range(4):
+            for d in range(5):
+                assert st[s_, r, d] == FP8_ALL[int(cq[0, s_, r, d])] * fr[s_, r]
 
 
 def _fp8_table():
@@ -485,6 +492,8 @@ MUTANTS = {
     "fp8 mantissa width": ("(1.0 + m / 8.0)", "(1.0 + m / 16.0)", "fp8.py"),
     "fp8 sign bit": ("np.where(c & 0x80, -1.0, 1.0)", "np.where(c & 0x40, -1.0, 1.0)", "fp8.py"),
     "fp8 scale of the wrong head": ("vals * s[:, :, None, None]", "vals * s[:, ::-1, None, None]", "fp8.py"),
+    "fp8 state factor of the wrong row": ("dtype=np.float64)[..., None]", "dtype=np.float64)[..., ::-1, None]",
+                                          "fp8.py"),
     # states.py
     "scale dropped": ("z = scale * (q @ k.T)", "z = (q @ k.T)"),
     "keys used as values": ("return p @ v, lse", "return p @ k, lse"),
