@@ -9,8 +9,9 @@
 // The kernels are HBM-bound: every byte of every input is read once, every output
 // byte written once. One lane owns 4 consecutive elements of one row (16 bytes of
 // fp32 OUT), or 8 of a bf16 OUT whose pointers are 16-byte aligned (else 4), so a
-// wave reads a contiguous run of 16-byte accesses per input per load instruction. Inputs whose weight is exactly zero (empty states) are neither read
-// nor added, and the accumulator starts at -0.0 (the additive identity of IEEE
+// wave reads a contiguous run of 16-byte accesses per input per load instruction. Inputs
+// whose weight is exactly zero (empty states) are not added (nor read, but for the first
+// four fp8 inputs of a row), and the accumulator starts at -0.0 (the additive identity of IEEE
 // arithmetic), so composing any state with empty states returns it bit for bit
 // (for fp32 OUT; a bf16 OUT is re-rounded, which is also exact for bf16 inputs).
 // Arithmetic is fp32 whatever the storage type; bf16 OUT is written rounded to
@@ -77,23 +78,30 @@ __device__ __forceinline__ f32x4 fp8x4_to_f32(unsigned w) {
   return f32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
-// 4*V consecutive OUT elements at element `off` (V = 2 for bf16: one 16-byte load; fp8:
-// V words of codes in one load).
-template <int IN, int V>
-__device__ __forceinline__ void loadv(const void* base, int64_t off, f32x4 (&x)[V]) {
+// 4*V E4M3 codes at element (= byte) `off`, as V words, in one load.
+template <int V>
+__device__ __forceinline__ void load_codes(const void* base, int64_t off, unsigned (&r)[V]) {
   const unsigned char* p8 = static_cast<const unsigned char*>(base) + off;
-  if constexpr (IN == kOutFP8 && V == 4) {
+  if constexpr (V == 4) {
     const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p8));
 #pragma unroll
-    for (int v = 0; v < 4; ++v) x[v] = fp8x4_to_f32(w[v]);
-  } else if constexpr (IN == kOutFP8 && V == 2) {
+    for (int v = 0; v < 4; ++v) r[v] = w[v];
+  } else if constexpr (V == 2) {
     const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p8));
-    x[0] = fp8x4_to_f32(w[0]);
-    x[V - 1] = fp8x4_to_f32(w[1]);
-  } else if constexpr (IN == kOutFP8) {
-    static_assert(V == 1, "fp8 loads of 4, 8 or 16 codes");
-    x[0] = fp8x4_to_f32(__builtin_nontemporal_load(reinterpret_cast<const unsigned*>(p8)));
-  } else if (IN == kOutBF16 && V == 2) {
+    r[0] = w[0];
+    r[V - 1] = w[1];
+  } else {
+    static_assert(V == 1, "4, 8 or 16 codes per load");
+    r[0] = __builtin_nontemporal_load(reinterpret_cast<const unsigned*>(p8));
+  }
+}
+
+// 4*V consecutive OUT elements at element `off` of fp32 or bf16 storage (V = 2 for bf16:
+// one 16-byte load; fp8 codes are read by load_codes).
+template <int IN, int V>
+__device__ __forceinline__ void loadv(const void* base, int64_t off, f32x4 (&x)[V]) {
+  static_assert(IN != kOutFP8, "fp8 codes are read by load_codes");
+  if (IN == kOutBF16 && V == 2) {
     const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(base) + off));
     x[0] = bf16_pair_to_f32(w[0], w[1]);
     x[V - 1] = bf16_pair_to_f32(w[2], w[3]);
@@ -239,6 +247,8 @@ __device__ __forceinline__ void store_fp8_row(const IO& io, int64_t row, int64_t
 // row's max, weights and their sum are reduced within the group, and the weights
 // are handed to the row's lanes through LDS (broadcast reads), so the streaming
 // loop issues only the OUT loads, with nontemporal hints (the inputs are read once).
+// Inputs whose weight is zero are not read, except the first four fp8 inputs of a row, whose
+// codes are loaded before the weights (and still not added).
 // fp8 states go through this path only (fp8 inputs: V = D / 32 up to 4, 4 to 16 codes per
 // lane; an fp8 OUT takes the lanes of its input's storage).
 template <int CPR, int V, int IN, int OUT, bool BATCHED>
@@ -252,13 +262,26 @@ __global__ __launch_bounds__(kMergeThreads) void merge_rows_kernel(const MergeAr
   const int g = lane / CPR, j = lane % CPR;     // row within the wave, lane within the row
   const int64_t row = (int64_t)blockIdx.x * RPB + wave * RPW + g;
   const bool live = row < a.rows;
-  // 1. LSE of inputs j, j + CPR, ... of this row; max over the row group
-  float Lv[AS_MAX_MERGE / CPR > 0 ? AS_MAX_MERGE / CPR : 1];
+  // 1. LSE of inputs j, j + CPR, ... of this row (and an fp8 input's row factor, loaded
+  // alongside, not after the weight); max over the row group
+  constexpr int NU = AS_MAX_MERGE / CPR > 0 ? AS_MAX_MERGE / CPR : 1;
+  const int64_t off = row * a.D + E * j;
+  // 0. fp8 inputs: the codes of the first 4 inputs, loaded before their weights are known
+  // (not added when the weight is zero), so that their latency overlaps step 1's
+  constexpr int U8 = 4;
+  unsigned r8[IN == kOutFP8 ? U8 : 1][V];
+  if constexpr (IN == kOutFP8) {
+#pragma unroll
+    for (int u = 0; u < U8; ++u)
+      if (live && u < io.n) load_codes<V>(io.out(u), off, r8[u]);
+  }
+  float Lv[NU], Fv[NU];
   float M = -INFINITY;
 #pragma unroll
   for (int u = 0; u < AS_MAX_MERGE / CPR; ++u) {
     const int k = j + u * CPR;
     Lv[u] = (live && k < io.n) ? io.lse(k)[row] : -INFINITY;
+    if constexpr (IN == kOutFP8) Fv[u] = (live && k < io.n) ? io.in_factor(k)[row] : 0.f;
     M = fmaxf(M, Lv[u]);
   }
 #pragma unroll
@@ -272,7 +295,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_rows_kernel(const MergeAr
     S += w;
     // an fp8 input's row factor scales its codes: folded into the weight of its OUT
     float wf = w;
-    if constexpr (IN == kOutFP8) wf = w != 0.f ? w * io.in_factor(k)[row] : 0.f;
+    if constexpr (IN == kOutFP8) wf = w * Fv[u];
     if (k < AS_MAX_MERGE) wsh[wave][g][k] = wf;
   }
 #pragma unroll
@@ -282,7 +305,6 @@ __global__ __launch_bounds__(kMergeThreads) void merge_rows_kernel(const MergeAr
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
   // (a row past the end is empty: its lanes leave here, all of a row group together)
   if (!live) return;
-  const int64_t off = row * a.D + E * j;
   f32x4 acc[V];
   if (empty) {   // (an fp8 OUT: codes 0 and factor 0)
 #pragma unroll
@@ -292,41 +314,75 @@ __global__ __launch_bounds__(kMergeThreads) void merge_rows_kernel(const MergeAr
     if (j == 0) io.dst_lse()[row] = -INFINITY;
     return;
   }
-  // 2. stream the inputs with non-zero weight
+  // 2. stream the inputs with non-zero weight, in input order
 #pragma unroll
   for (int v = 0; v < V; ++v) acc[v] = f32x4{-0.f, -0.f, -0.f, -0.f};
   int k = 0;
-  for (; k + 4 <= io.n; k += 4) {
-    float w[4];
-    f32x4 x[4][V];
+  if constexpr (IN == kOutFP8) {
+    // fp8 inputs, 4 at a time: the codes of the next 4 are loaded before the current 4 are
+    // widened and added (raw code words: V registers per input)
+    for (; k < io.n; k += U8) {
+      unsigned nx[U8][V];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) w[u] = wsh[wave][g][k + u];
+      for (int u = 0; u < U8; ++u) {
+        const int kk = k + U8 + u;
+        if (kk < io.n && wsh[wave][g][kk] != 0.f) load_codes<V>(io.out(kk), off, nx[u]);
+        else {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (w[u] != 0.f) loadv<IN, V>(io.out(k + u), off, x[u]);
-      else {
-#pragma unroll
-        for (int v = 0; v < V; ++v) x[u][v] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int v = 0; v < V; ++v) nx[u][v] = 0u;
+        }
       }
-    }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (w[u] != 0.f) {
+      for (int u = 0; u < U8; ++u) {
+        const int kk = k + u;
+        const float w = kk < io.n ? wsh[wave][g][kk] : 0.f;
+        if (w != 0.f) {
+#pragma unroll
+          for (int v = 0; v < V; ++v) {
+            const f32x4 x = fp8x4_to_f32(r8[u][v]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[v][e] = __builtin_fmaf(w, x[e], acc[v][e]);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U8; ++u)
+#pragma unroll
+        for (int v = 0; v < V; ++v) r8[u][v] = nx[u][v];
+    }
+  } else {
+    for (; k + 4 <= io.n; k += 4) {
+      float w[4];
+      f32x4 x[4][V];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) w[u] = wsh[wave][g][k + u];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (w[u] != 0.f) loadv<IN, V>(io.out(k + u), off, x[u]);
+        else {
+#pragma unroll
+          for (int v = 0; v < V; ++v) x[u][v] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (w[u] != 0.f) {
+#pragma unroll
+          for (int v = 0; v < V; ++v)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[v][e] = __builtin_fmaf(w[u], x[u][v][e], acc[v][e]);
+        }
+    }
+    for (; k < io.n; ++k) {
+      const float w = wsh[wave][g][k];
+      if (w != 0.f) {
+        f32x4 x[V];
+        loadv<IN, V>(io.out(k), off, x);
 #pragma unroll
         for (int v = 0; v < V; ++v)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[v][e] = __builtin_fmaf(w[u], x[u][v][e], acc[v][e]);
+          for (int e = 0; e < 4; ++e) acc[v][e] = __builtin_fmaf(w, x[v][e], acc[v][e]);
       }
-  }
-  for (; k < io.n; ++k) {
-    const float w = wsh[wave][g][k];
-    if (w != 0.f) {
-      f32x4 x[V];
-      loadv<IN, V>(io.out(k), off, x);
-#pragma unroll
-      for (int v = 0; v < V; ++v)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[v][e] = __builtin_fmaf(w, x[v][e], acc[v][e]);
     }
   }
 #pragma unroll
