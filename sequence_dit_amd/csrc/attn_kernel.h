@@ -102,7 +102,9 @@ struct Tile {
   static constexpr int NKB = KB / 32;             // 32-key MFMA blocks per tile
 };
 constexpr int kThreads = kWaves * 64;
-constexpr float kRescaleThreshold = 64.0f;   // log2 units: probabilities stay <= 2^64
+// Probabilities of a tile may reach 2^64 before the running max is moved (the sum of a
+// lane's 32 or 64 of them then stays far inside fp32, and so do O and l).
+constexpr float kRescaleLimit = 18446744073709551616.0f;   // 2^64
 
 // Maps the hardware workgroup id to a logical tile id so that consecutive logical
 // ids land on the same XCD (workgroups are dealt round-robin over the 8 XCDs).
@@ -353,11 +355,8 @@ struct Wave {
   }
 
   // The running max m only has to keep the probabilities finite (p <= 2^64 here):
-  // floating point does not care how far below 1 they are. Each lane compares its
-  // own scores against m + 64 (one max3 chain, no cross-lane step); only when some
-  // lane exceeds it (always on the first tile, where m = -inf) does the wave take
-  // the exact row max, rescale O and l, and move m. O and l always share m, so
-  // OUT = O / l and LSE = m + log2 l are exact whichever m is used.
+  // floating point does not care how far below 1 they are. O and l always share m,
+  // so OUT = O / l and LSE = m + log2 l are exact whichever m is used.
   template <bool MASK>
   __device__ __forceinline__ void softmax(int valid, float c2, int half) {
     if (MASK) {  // keys past the end of the partition
@@ -370,6 +369,28 @@ struct Wave {
       mask_tail(valid, c2, half);
       c2 = 1.0f;
     }
+    // Exponentiate first: the probabilities of the tile are taken with the running max
+    // as it stands, and only when some lane's sum of them exceeds 2^64 or is not finite
+    // (a score more than 64 above m), or on the row's first tile (m = -inf), is the tile
+    // taken again after moving m to the exact row max. The common tile then needs no
+    // max over its scores.
+    const bool fresh = __builtin_amdgcn_ballot_w64(m == -INFINITY) != 0;   // wave-uniform
+    float t = 0.f;
+    bool redo = fresh;
+    if (!fresh) {
+      t = exp_pass(c2);
+      redo = __builtin_amdgcn_ballot_w64(!(t <= kRescaleLimit)) != 0;
+    }
+    if (redo) {
+      move_max(c2);
+      t = exp_pass(c2);
+    }
+    l += t;
+    if (GR) lp += t;
+  }
+
+  // m <- max(m, the exact row max of the tile's scaled scores); O, l (and lp) rescaled.
+  __device__ __forceinline__ void move_max(float c2) {
     float x = s[0][0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) x = fmaxf(x, s[0][r]);
@@ -377,23 +398,25 @@ struct Wave {
     for (int kb = 1; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) x = fmaxf(x, s[kb][r]);
-    if (__builtin_amdgcn_ballot_w64(x * c2 > m + kRescaleThreshold) != 0) {
-      const float mx = wave_max_halves(x) * c2;
-      const float mn = fmaxf(m, mx);
-      const float f = __builtin_amdgcn_exp2f(m - mn);   // 0 on the first tile (m = -inf)
-      m = mn;
-      l *= f;
-      if (GR) lp *= f;
-      // in-place multiplies keep the accumulators in their registers across the branch
+    const float mx = wave_max_halves(x) * c2;
+    const float mn = fmaxf(m, mx);
+    const float f = __builtin_amdgcn_exp2f(m - mn);   // 0 on the first tile (m = -inf)
+    m = mn;
+    l *= f;
+    if (GR) lp *= f;
+    // in-place multiplies keep the accumulators in their registers across the branch
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) asm volatile("v_mul_f32 %0, %0, %1" : "+v"(o[db][r]) : "v"(f));
-    }
+      for (int r = 0; r < 16; ++r) asm volatile("v_mul_f32 %0, %0, %1" : "+v"(o[db][r]) : "v"(f));
+  }
+
+  // P = exp2(c2 s - m) of the tile into pf (bf16); returns this lane's sum of the fp32
+  // probabilities (summing their bf16 roundings would put the bf16 unit roundoff, 2^-8,
+  // straight into LSE).
+  __device__ __forceinline__ float exp_pass(float c2) {
     const float nm = -m;
-    // the row sum uses the fp32 probabilities: summing their bf16 roundings
-    // would put the bf16 unit roundoff (2^-8) straight into LSE
-    float acc0 = GR ? 0.f : l, acc1 = 0.f;
+    float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -413,13 +436,7 @@ struct Wave {
         // compiler sinks it past the barrier into the next MFMA phase, next to its use)
         if (GR) asm volatile("" : "+v"(pf[kb][c]));
       }
-    if (GR) {
-      const float t = acc0 + acc1;
-      l += t;
-      lp += t;
-    } else {
-      l = acc0 + acc1;
-    }
+    return acc0 + acc1;
   }
 };
 
