@@ -588,6 +588,47 @@ struct Stager {
   }
 };
 
+// fp32 OUT of a wave's 32 rows: a lane holds 4-value pieces of one row (val(db, j): d =
+// 32 db + 8 j + 4 half of row l32); stored as they are, every store instruction would
+// write 32-byte pieces of 32 rows. Once the schedule's last barrier is passed the tile
+// slots are free: each wave passes its rows through its own LDS region, DH values of d
+// at a time, and reads them back by rows, so that every store writes whole DH * 4-byte
+// row segments (256 or 128 bytes), streamed past the caches (nontemporal: written once).
+// rows: the wave's rows inside the output (the others are not stored); out_rows: its
+// first row.
+template <int D, bool QK8, typename F>
+__device__ __forceinline__ void store_rows_f32(char* smem, int wave, int lane, float* out_rows, int rows, F val) {
+  using L = Lds<D, QK8>;
+  constexpr int DH = QK8 ? 32 : 64;        // d per pass (the fp8 kernel's LDS is smaller)
+  constexpr int RP = DH * 4 + 16;          // LDS row pitch, bytes
+  constexpr int LPR = DH / 4;              // lanes per row when reading back
+  constexpr int RPI = 64 / LPR;            // rows per read
+  static_assert(kWaves * kRowsPerWave * RP <= L::BYTES, "epilogue staging fits the tile slots");
+  const int l32 = lane & 31, half = lane >> 5;
+  char* reg = smem + wave * kRowsPerWave * RP;
+#pragma unroll
+  for (int pass = 0; pass < D / DH; ++pass) {
+#pragma unroll
+    for (int db = pass * DH / 32; db < (pass + 1) * DH / 32; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<f32x4*>(reg + l32 * RP + ((db * 32 - pass * DH) + 8 * j + 4 * half) * 4) = val(db, j);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+#pragma unroll
+    for (int it = 0; it < kRowsPerWave / RPI; ++it) {
+      const int row = it * RPI + lane / LPR, col = lane % LPR;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(reg + row * RP + col * 16);
+      if (row < rows) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(out_rows + (int64_t)row * D + pass * DH + col * 4));
+    }
+    // the next pass rewrites the region: its reads are complete first
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  }
+}
+
 // Schedule ("ping-pong"): the 8 waves form two groups of 4, one wave of each group
 // per SIMD. Every wave alternates an MFMA phase X_t (S_t = K_t Q^T and
 // O += V_{t-1} P_{t-1}^T) with a VALU phase Y_t (softmax of S_t -> P_t, plus tile
@@ -906,42 +947,39 @@ void attn_bf16_kernel(const AttnArgs a) {
 
     // ---- epilogue: the group's composed state, composed with the given state for group 0
     const float lt = wave_sum_halves(w.l);
-    if (qrow < a.Sq) {
-      // weight of O (fp8 V: O is in units of V's factor)
-      float wo = lt > 0.f ? (V8 ? a.v_scale[bh] : 1.0f) / lt : 0.f;
-      float L = lt > 0.f ? (w.m + __log2f(lt)) * 0.69314718055994530942f : -INFINITY;
-      float wc = 0.f;                          // weight of the given state's OUT
-      const bool fold = a.fold_out != nullptr && part == 0;
-      const int64_t frow = (int64_t)bh * a.Sq + qrow;   // row of the given [B][H][Sq] state
-      if (fold) {
-        const float Lc = a.fold_lse[frow];
-        const float M = fmaxf(L, Lc);
-        if (M == -INFINITY) {
-          wo = 0.f;
-          L = -INFINITY;
-        } else {
-          const float e1 = expf(L - M), e2 = expf(Lc - M), S = e1 + e2;
-          wo *= e1 / S;
-          wc = e2 / S;
-          L = M + logf(S);
-        }
+    // weight of O (fp8 V: O is in units of V's factor)
+    float wo = lt > 0.f ? (V8 ? a.v_scale[bh] : 1.0f) / lt : 0.f;
+    float L = lt > 0.f ? (w.m + __log2f(lt)) * 0.69314718055994530942f : -INFINITY;
+    float wc = 0.f;                            // weight of the given state's OUT
+    const bool fold = a.fold_out != nullptr && part == 0 && qrow < a.Sq;
+    const int64_t frow = (int64_t)bh * a.Sq + qrow;   // row of the given [B][H][Sq] state
+    if (fold) {
+      const float Lc = a.fold_lse[frow];
+      const float M = fmaxf(L, Lc);
+      if (M == -INFINITY) {
+        wo = 0.f;
+        L = -INFINITY;
+      } else {
+        const float e1 = expf(L - M), e2 = expf(Lc - M), S = e1 + e2;
+        wo *= e1 / S;
+        wc = e2 / S;
+        L = M + logf(S);
       }
-      const int64_t orow = (row_base + qrow) * D;
-#pragma unroll
-      for (int db = 0; db < W::NDB; ++db)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int d = db * 32 + 8 * j + 4 * half;
-          f32x4 val = {w.o[db][4 * j] * wo, w.o[db][4 * j + 1] * wo, w.o[db][4 * j + 2] * wo, w.o[db][4 * j + 3] * wo};
-          if (fold) {
-            const f32x4 c = *reinterpret_cast<const f32x4*>(a.fold_out + frow * D + d);
-            val = f32x4{__builtin_fmaf(wc, c[0], val[0]), __builtin_fmaf(wc, c[1], val[1]),
-                        __builtin_fmaf(wc, c[2], val[2]), __builtin_fmaf(wc, c[3], val[3])};
-          }
-          store_out4<kOutF32>(a.out, orow + d, val);
-        }
-      if (half == 0) lse[qrow] = L;
     }
+    const int w0 = q0 + wave * kRowsPerWave;     // the wave's first row
+    store_rows_f32<D, QK8>(smem, wave, lane, static_cast<float*>(a.out) + (row_base + w0) * D, a.Sq - w0,
+                           [&](int db, int j) __attribute__((always_inline)) {
+                             f32x4 val = {w.o[db][4 * j] * wo, w.o[db][4 * j + 1] * wo, w.o[db][4 * j + 2] * wo,
+                                          w.o[db][4 * j + 3] * wo};
+                             if (fold) {
+                               const f32x4 c = *reinterpret_cast<const f32x4*>(a.fold_out + frow * D + db * 32 +
+                                                                               8 * j + 4 * half);
+                               val = f32x4{__builtin_fmaf(wc, c[0], val[0]), __builtin_fmaf(wc, c[1], val[1]),
+                                           __builtin_fmaf(wc, c[2], val[2]), __builtin_fmaf(wc, c[3], val[3])};
+                             }
+                             return val;
+                           });
+    if (half == 0 && qrow < a.Sq) lse[qrow] = L;
   } else {
     const int ks = a.ranges[2 * part];
     T = (n + KB - 1) / KB;
@@ -981,6 +1019,14 @@ void attn_bf16_kernel(const AttnArgs a) {
           lse[qrow] = (w.m + __log2f(lt)) * 0.69314718055994530942f;
         }
       }
+    } else if constexpr (OUT == kOutF32) {
+      const int w0 = q0 + wave * kRowsPerWave;   // the wave's first row
+      store_rows_f32<D, QK8>(smem, wave, lane, static_cast<float*>(a.out) + (row_base + w0) * D, a.Sq - w0,
+                             [&](int db, int j) __attribute__((always_inline)) {
+                               return f32x4{w.o[db][4 * j] * inv, w.o[db][4 * j + 1] * inv,
+                                            w.o[db][4 * j + 2] * inv, w.o[db][4 * j + 3] * inv};
+                             });
+      if (half == 0 && qrow < a.Sq) lse[qrow] = (w.m + __log2f(lt)) * 0.69314718055994530942f;
     } else if (qrow < a.Sq) {
       const int64_t orow = (row_base + qrow) * D;
 #pragma unroll
