@@ -588,39 +588,50 @@ struct Stager {
   }
 };
 
-// fp32 OUT of a wave's 32 rows: a lane holds 4-value pieces of one row (val(db, j): d =
-// 32 db + 8 j + 4 half of row l32); stored as they are, every store instruction would
-// write 32-byte pieces of 32 rows. Once the schedule's last barrier is passed the tile
-// slots are free: each wave passes its rows through its own LDS region, DH values of d
-// at a time, and reads them back by rows, so that every store writes whole DH * 4-byte
-// row segments (256 or 128 bytes), streamed past the caches (nontemporal: written once).
-// rows: the wave's rows inside the output (the others are not stored); out_rows: its
-// first row.
-template <int D, bool QK8, typename F>
-__device__ __forceinline__ void store_rows_f32(char* smem, int wave, int lane, float* out_rows, int rows, F val) {
+// OUT of a wave's 32 rows, ESZ bytes per element (4: fp32, 2: bf16, 1: fp8 codes): a lane
+// holds 4-element pieces of one row (piece(db, j): d = 32 db + 8 j + 4 half of row l32, as
+// one 16-, 8- or 4-byte value); stored as they are, every store instruction would write
+// small pieces of 32 rows. Once the schedule's last barrier is passed the tile slots are
+// free: each wave passes its rows through its own LDS region, PB bytes of a row at a time,
+// and reads them back by rows, so that every store writes whole PB-byte row segments
+// (128 or 256 bytes), streamed past the caches (nontemporal: written once).
+// rows: the wave's rows inside the output (the others are not stored); out_rows: the
+// first one; row_bytes: the output's row pitch.
+template <int D, bool QK8, int ESZ, typename F>
+__device__ __forceinline__ void store_rows(char* smem, int wave, int lane, char* out_rows, int rows, F piece) {
   using L = Lds<D, QK8>;
-  constexpr int DH = QK8 ? 32 : 64;        // d per pass (the fp8 kernel's LDS is smaller)
-  constexpr int RP = DH * 4 + 16;          // LDS row pitch, bytes
-  constexpr int LPR = DH / 4;              // lanes per row when reading back
-  constexpr int RPI = 64 / LPR;            // rows per read
-  static_assert(kWaves * kRowsPerWave * RP <= L::BYTES, "epilogue staging fits the tile slots");
+  constexpr int RB = D * ESZ;                                 // bytes of a row
+  constexpr int PB = kWaves * kRowsPerWave * (RB + 16) <= L::BYTES ? RB
+                     : kWaves * kRowsPerWave * (RB / 2 + 16) <= L::BYTES ? RB / 2 : RB / 4;
+  constexpr int RP = PB + 16;                                 // LDS row pitch
+  constexpr int LPR = PB / 16;                                // lanes per row when reading back
+  constexpr int RPI = 64 / LPR;                               // rows per read
+  constexpr int NDB = D / 32;
+  static_assert(kWaves * kRowsPerWave * RP <= L::BYTES && RPI >= 1 && kRowsPerWave % RPI == 0, "epilogue staging");
   const int l32 = lane & 31, half = lane >> 5;
   char* reg = smem + wave * kRowsPerWave * RP;
 #pragma unroll
-  for (int pass = 0; pass < D / DH; ++pass) {
+  for (int pass = 0; pass < RB / PB; ++pass) {
 #pragma unroll
-    for (int db = pass * DH / 32; db < (pass + 1) * DH / 32; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<f32x4*>(reg + l32 * RP + ((db * 32 - pass * DH) + 8 * j + 4 * half) * 4) = val(db, j);
+      for (int j = 0; j < 4; ++j) {
+        const int off = (db * 32 + 8 * j) * ESZ - pass * PB;   // the piece pair's first byte in the pass
+        if (off >= 0 && off < PB) {
+          const auto v = piece(db, j);
+          using P = std::remove_cv_t<decltype(v)>;
+          *reinterpret_cast<P*>(reg + l32 * RP + off + 4 * ESZ * half) = v;
+        }
+      }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 #pragma unroll
     for (int it = 0; it < kRowsPerWave / RPI; ++it) {
       const int row = it * RPI + lane / LPR, col = lane % LPR;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(reg + row * RP + col * 16);
-      if (row < rows) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(out_rows + (int64_t)row * D + pass * DH + col * 4));
+      const u32x4 v = *reinterpret_cast<const u32x4*>(reg + row * RP + col * 16);
+      if (row < rows)
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out_rows + (int64_t)row * RB + pass * PB + col * 16));
     }
     // the next pass rewrites the region: its reads are complete first
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
@@ -967,7 +978,7 @@ void attn_bf16_kernel(const AttnArgs a) {
       }
     }
     const int w0 = q0 + wave * kRowsPerWave;     // the wave's first row
-    store_rows_f32<D, QK8>(smem, wave, lane, static_cast<float*>(a.out) + (row_base + w0) * D, a.Sq - w0,
+    store_rows<D, QK8, 4>(smem, wave, lane, reinterpret_cast<char*>(static_cast<float*>(a.out) + (row_base + w0) * D), a.Sq - w0,
                            [&](int db, int j) __attribute__((always_inline)) {
                              f32x4 val = {w.o[db][4 * j] * wo, w.o[db][4 * j + 1] * wo, w.o[db][4 * j + 2] * wo,
                                           w.o[db][4 * j + 3] * wo};
@@ -1001,43 +1012,35 @@ void attn_bf16_kernel(const AttnArgs a) {
         for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(w.o[db][e]));
       const float amax = wave_max_halves(mx) * fabsf(inv);   // = max |O * inv|: rounding is monotone
       const float qf = amax > 0.f ? 448.0f / amax : 0.f;
-      if (qrow < a.Sq) {
-        char* pay = static_cast<char*>(a.out) + (int64_t)part * a.payload_bytes;
-        const int64_t srow = (int64_t)bh * a.Sq + qrow;
-        unsigned char* crow = reinterpret_cast<unsigned char*>(pay) + srow * D;
-#pragma unroll
-        for (int db = 0; db < W::NDB; ++db)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float x[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = clamp448((w.o[db][4 * j + e] * inv) * qf);
-            *reinterpret_cast<unsigned*>(crow + db * 32 + 8 * j + 4 * half) = fp8x4(x[0], x[1], x[2], x[3]);
-          }
-        if (half == 0) {
-          reinterpret_cast<float*>(pay + a.state_rows * D)[srow] = amax / 448.0f;
-          lse[qrow] = (w.m + __log2f(lt)) * 0.69314718055994530942f;
-        }
-      }
-    } else if constexpr (OUT == kOutF32) {
+      char* pay = static_cast<char*>(a.out) + (int64_t)part * a.payload_bytes;
       const int w0 = q0 + wave * kRowsPerWave;   // the wave's first row
-      store_rows_f32<D, QK8>(smem, wave, lane, static_cast<float*>(a.out) + (row_base + w0) * D, a.Sq - w0,
-                             [&](int db, int j) __attribute__((always_inline)) {
-                               return f32x4{w.o[db][4 * j] * inv, w.o[db][4 * j + 1] * inv,
-                                            w.o[db][4 * j + 2] * inv, w.o[db][4 * j + 3] * inv};
-                             });
+      store_rows<D, QK8, 1>(smem, wave, lane, pay + ((int64_t)bh * a.Sq + w0) * D, a.Sq - w0,
+                            [&](int db, int j) __attribute__((always_inline)) {
+                              float x[4];
+#pragma unroll
+                              for (int e = 0; e < 4; ++e) x[e] = clamp448((w.o[db][4 * j + e] * inv) * qf);
+                              return fp8x4(x[0], x[1], x[2], x[3]);
+                            });
+      if (half == 0 && qrow < a.Sq) {
+        reinterpret_cast<float*>(pay + a.state_rows * D)[(int64_t)bh * a.Sq + qrow] = amax / 448.0f;
+        lse[qrow] = (w.m + __log2f(lt)) * 0.69314718055994530942f;
+      }
+    } else {
+      // fp32 or bf16 (rounded to nearest even) OUT
+      constexpr int ESZ = OUT == kOutBF16 ? 2 : 4;
+      const int w0 = q0 + wave * kRowsPerWave;   // the wave's first row
+      store_rows<D, QK8, ESZ>(smem, wave, lane, static_cast<char*>(a.out) + (row_base + w0) * D * ESZ, a.Sq - w0,
+                              [&](int db, int j) __attribute__((always_inline)) {
+                                const f32x4 v = {w.o[db][4 * j] * inv, w.o[db][4 * j + 1] * inv,
+                                                 w.o[db][4 * j + 2] * inv, w.o[db][4 * j + 3] * inv};
+                                if constexpr (OUT == kOutBF16) {
+                                  const bf16x4 h = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+                                  return __builtin_bit_cast(u32x2, h);
+                                } else {
+                                  return v;
+                                }
+                              });
       if (half == 0 && qrow < a.Sq) lse[qrow] = (w.m + __log2f(lt)) * 0.69314718055994530942f;
-    } else if (qrow < a.Sq) {
-      const int64_t orow = (row_base + qrow) * D;
-#pragma unroll
-      for (int db = 0; db < W::NDB; ++db)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f32x4 val = {w.o[db][4 * j] * inv, w.o[db][4 * j + 1] * inv, w.o[db][4 * j + 2] * inv,
-                             w.o[db][4 * j + 3] * inv};
-          store_out4<OUT>(a.out, orow + db * 32 + 8 * j + 4 * half, val);
-        }
-      if (half == 0) lse[qrow] = (w.m + __log2f(lt)) * 0.69314718055994530942f;
     }
   }
 }
