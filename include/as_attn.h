@@ -240,7 +240,12 @@ as_status as_partition_attn_fp8_qkv(const void* q, const void* k, const void* v,
  *               both NULL: a state composed into group 0's result as as_merge would.
  * out, lse      DEVICE float32 [G][B][H][Sq][D] (16-byte aligned) and [G][B][H][Sq].
  * part_lse      DEVICE float32 [P][B][H][Sq] or NULL: the LSE of every partition, equal to
- *               as_partition_attn's lse (e.g. for as_partition_contribution).
+ *               as_partition_attn's lse (e.g. for as_partition_contribution) up to rounding,
+ *               with one exception: a partition's sum is taken against the running max of
+ *               its group, so a partition whose every score lies more than 87 below the
+ *               largest score of the earlier keys of its group (weight under e^-87 of
+ *               theirs, below fp32's normal range either way) may come out smaller, down
+ *               to -inf.
  * Outputs must not overlap each other or any input (checked). All other arguments and
  * rules are as for as_partition_attn.
  */

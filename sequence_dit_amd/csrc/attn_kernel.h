@@ -326,6 +326,8 @@ struct Wave {
 
   // Softmax phase of tile t: online softmax of S_t (exp2 domain, lazy rescale) -> P_t.
   // valid = keys of the tile inside the partition.
+  // FIRST: the row's first tile (of the partition, or of the group in grouped launches).
+  template <bool FIRST>
   __device__ __forceinline__ void softmax_phase(int valid, float c2, int half) {
     if constexpr (GR) {
       // Grouped launches meet masked tiles inside the tile loop (at every partition end):
@@ -336,11 +338,11 @@ struct Wave {
         mask_tail(valid, c2, half);
         c2 = 1.0f;
       }
-      softmax<false>(valid, c2, half);
+      softmax<false, FIRST>(valid, c2, half);
     } else {
       // single partition: the masked tile is the last one, outside the steady-state loop
-      if (valid < KB) softmax<true>(valid, c2, half);
-      else softmax<false>(valid, c2, half);
+      if (valid < KB) softmax<true, FIRST>(valid, c2, half);
+      else softmax<false, FIRST>(valid, c2, half);
     }
   }
 
@@ -357,7 +359,7 @@ struct Wave {
   // The running max m only has to keep the probabilities finite (p <= 2^64 here):
   // floating point does not care how far below 1 they are. O and l always share m,
   // so OUT = O / l and LSE = m + log2 l are exact whichever m is used.
-  template <bool MASK>
+  template <bool MASK, bool FIRST>
   __device__ __forceinline__ void softmax(int valid, float c2, int half) {
     if (MASK) {  // keys past the end of the partition
       // The mask is applied to scaled scores and the rest of the tile then runs with
@@ -370,20 +372,20 @@ struct Wave {
       c2 = 1.0f;
     }
     // Exponentiate first: the probabilities of the tile are taken with the running max
-    // as it stands, and only when some lane's sum of them exceeds 2^64 or is not finite
-    // (a score more than 64 above m), or on the row's first tile (m = -inf), is the tile
-    // taken again after moving m to the exact row max. The common tile then needs no
-    // max over its scores.
-    const bool fresh = __builtin_amdgcn_ballot_w64(m == -INFINITY) != 0;   // wave-uniform
-    float t = 0.f;
-    bool redo = fresh;
-    if (!fresh) {
-      t = exp_pass(c2);
-      redo = __builtin_amdgcn_ballot_w64(!(t <= kRescaleLimit)) != 0;
-    }
-    if (redo) {
+    // as it stands; only when some lane's sum of them exceeds 2^64 or is not finite (a
+    // score more than 64 above m) is the tile taken again after moving m to the exact row
+    // max. The row's first tile (m = -inf) moves m first. The common tile then needs no
+    // max over its scores, and one vote of the wave.
+    float t;
+    if constexpr (FIRST) {
       move_max(c2);
       t = exp_pass(c2);
+    } else {
+      t = exp_pass(c2);
+      if (__builtin_amdgcn_ballot_w64(!(t <= kRescaleLimit)) != 0) {
+        move_max(c2);
+        t = exp_pass(c2);
+      }
     }
     l += t;
     if (GR) lp += t;
@@ -404,11 +406,10 @@ struct Wave {
     m = mn;
     l *= f;
     if (GR) lp *= f;
-    // in-place multiplies keep the accumulators in their registers across the branch
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) asm volatile("v_mul_f32 %0, %0, %1" : "+v"(o[db][r]) : "v"(f));
+      for (int r = 0; r < 16; ++r) o[db][r] *= f;
   }
 
   // P = exp2(c2 s - m) of the tile into pf (bf16); returns this lane's sum of the fp32
@@ -842,10 +843,14 @@ void attn_bf16_kernel(const AttnArgs a) {
     if constexpr (GROUPED) st.load_v_from(st.next_rsrc());
     else st.load_v(tile);
   };
-  auto SMX = [&](int tile) __attribute__((always_inline)) {
+  auto SMX = [&](int tile, auto FIRSTC) __attribute__((always_inline)) {
+    constexpr bool FIRST = decltype(FIRSTC)::value;
     if constexpr (GROUPED) {
-      w.softmax_phase(sc.valid(), c2, half);
+      w.template softmax_phase<FIRST>(sc.valid(), c2, half);
       if (sc.last_of_partition()) {
+        // The partition's sum is taken against the group's running max: a partition whose
+        // every score lies more than 126 below it (log2 units) sums to 0 here, and its LSE
+        // comes out as -inf (its weight against the group's is under 2^-126 either way).
         const float lp = wave_sum_halves(w.lp);
         if (a.part_lse && qrow < a.Sq && half == 0) {
           const int orig = sc.index();   // the caller's partition index
@@ -855,7 +860,7 @@ void attn_bf16_kernel(const AttnArgs a) {
       }
       sc.advance();
     } else {
-      w.softmax_phase(n - tile * KB, c2, half);
+      w.template softmax_phase<FIRST>(n - tile * KB, c2, half);
     }
   };
 
@@ -876,7 +881,7 @@ void attn_bf16_kernel(const AttnArgs a) {
       lds_barrier();
       if constexpr (ON) w.template mfma_phase<0, 0, true, false>(smem);  // X_0
       lds_barrier();
-      if constexpr (ON) SMX(0);                    // Y_0
+      if constexpr (ON) SMX(0, std::true_type{});                    // Y_0
       if (T > 2) st.template store_k<0>(smem);
       LDK(3);
       lds_barrier();
@@ -884,13 +889,13 @@ void attn_bf16_kernel(const AttnArgs a) {
       for (; t + 1 < T; t += 2) {
         if constexpr (ON) w.template mfma_phase<1, 0, true, true>(smem);     // X_t, t odd
         lds_barrier();
-        if constexpr (ON) SMX(t);
+        if constexpr (ON) SMX(t, std::false_type{});
         if (t + 2 < T) st.template store_k<1>(smem);
         LDK(t + 3);
         lds_barrier();
         if constexpr (ON) w.template mfma_phase<0, 1, true, true>(smem);     // X_{t+1}, even
         lds_barrier();
-        if constexpr (ON) SMX(t + 1);
+        if constexpr (ON) SMX(t + 1, std::false_type{});
         if (t + 3 < T) st.template store_k<0>(smem);
         LDK(t + 4);
         lds_barrier();
@@ -898,7 +903,7 @@ void attn_bf16_kernel(const AttnArgs a) {
       if (t < T) {  // t odd, last tile
         if constexpr (ON) w.template mfma_phase<1, 0, true, true>(smem);
         lds_barrier();
-        if constexpr (ON) SMX(t);
+        if constexpr (ON) SMX(t, std::false_type{});
         lds_barrier();
         if constexpr (ON) w.template mfma_phase<0, 1, false, true>(smem);    // X_T, V slot (T-1)&1 = 1
       } else {      // T even (or 1): V slot (T-1)&1
@@ -913,7 +918,7 @@ void attn_bf16_kernel(const AttnArgs a) {
       lds_barrier();
       if constexpr (ON) w.template mfma_phase<0, 0, true, false>(smem);  // X_0
       lds_barrier();
-      if constexpr (ON) SMX(0);                    // Y_0
+      if constexpr (ON) SMX(0, std::true_type{});                    // Y_0
       st.template store_v<0>(smem);
       LDV(1);
       lds_barrier();
@@ -921,13 +926,13 @@ void attn_bf16_kernel(const AttnArgs a) {
       for (; t + 1 < T; t += 2) {
         if constexpr (ON) w.template mfma_phase<1, 0, true, true>(smem);
         lds_barrier();
-        if constexpr (ON) SMX(t);
+        if constexpr (ON) SMX(t, std::false_type{});
         st.template store_v<1>(smem);
         LDV(t + 1);
         lds_barrier();
         if constexpr (ON) w.template mfma_phase<0, 1, true, true>(smem);
         lds_barrier();
-        if constexpr (ON) SMX(t + 1);
+        if constexpr (ON) SMX(t + 1, std::false_type{});
         st.template store_v<0>(smem);
         LDV(t + 2);
         lds_barrier();
@@ -935,7 +940,7 @@ void attn_bf16_kernel(const AttnArgs a) {
       if (t < T) {
         if constexpr (ON) w.template mfma_phase<1, 0, true, true>(smem);
         lds_barrier();
-        if constexpr (ON) SMX(t);
+        if constexpr (ON) SMX(t, std::false_type{});
         st.template store_v<1>(smem);
         lds_barrier();
         if constexpr (ON) w.template mfma_phase<0, 1, false, true>(smem);
