@@ -347,13 +347,27 @@ struct Wave {
   }
 
   // Keys at or past `valid` of the tile: scores scaled by c2, masked ones set to -inf.
+  // Single-partition launches: a 32-key block wholly inside or wholly past the end (a
+  // wave-uniform test) is scaled or cleared without a comparison per key. (Grouped launches
+  // mask inside the tile loop, where the three-way branch costs more than it saves.)
   __device__ __forceinline__ void mask_tail(int valid, float c2, int half) {
     const int lim = valid - 4 * half;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NKB; ++kb) {
+      if (GR) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        s[kb][r] = (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) ? -INFINITY : s[kb][r] * c2;
+        for (int r = 0; r < 16; ++r) s[kb][r] = (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) ? -INFINITY : s[kb][r] * c2;
+      } else if (kb * 32 + 32 <= valid) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] *= c2;
+      } else if (kb * 32 >= valid) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = -INFINITY;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) ? -INFINITY : s[kb][r] * c2;
+      }
+    }
   }
 
   // The running max m only has to keep the probabilities finite (p <= 2^64 here):
