@@ -274,7 +274,7 @@ as_status attn_impl(const void* q, const void* k, const void* v, as_dtype dtype,
   if (dtype == AS_BF16) {
     const int bq = as::attn_bf16_rows_per_block((int)D);
     a.n_qtiles = (int32_t)((Sq + bq - 1) / bq);
-    if ((int64_t)a.n_qtiles * B * H * P > 0x7fffffff) return fail(AS_ERR_UNSUPPORTED, "grid too large");
+    if ((B * H * P + 7) / 8 * 8 * a.n_qtiles > 0x7fffffff) return fail(AS_ERR_UNSUPPORTED, "grid too large");
     return hip_status(as::launch_attn_bf16(a, stream), "partition_attn bf16 launch");
   }
   const int bq = as::attn_f32_rows_per_block((int)D);

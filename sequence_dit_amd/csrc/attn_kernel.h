@@ -106,15 +106,6 @@ constexpr int kThreads = kWaves * 64;
 // lane's 32 or 64 of them then stays far inside fp32, and so do O and l).
 constexpr float kRescaleLimit = 18446744073709551616.0f;   // 2^64
 
-// Maps the hardware workgroup id to a logical tile id so that consecutive logical
-// ids land on the same XCD (workgroups are dealt round-robin over the 8 XCDs).
-__device__ __forceinline__ int xcd_remap(int L, int total) {
-  constexpr int kXcd = 8;
-  const int per = total / kXcd, rem = total % kXcd;
-  const int x = L % kXcd, idx = L / kXcd;
-  return (x < rem) ? x * (per + 1) + idx : rem * (per + 1) + (x - rem) * per + idx;
-}
-
 __device__ __forceinline__ float wave_max_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -690,25 +681,30 @@ void attn_bf16_kernel(const AttnArgs a) {
   // grouped launches: (first key, keys, caller's index) of every partition of the group
   __shared__ int gtab[GROUPED ? 3 * AS_MAX_PARTITIONS : 1];
 
+  // Units (partition or group, b, h) are dealt round-robin over the 8 XCDs (workgroup i
+  // runs on XCD i % 8) and the query tiles of a unit run consecutively on its XCD, whose L2
+  // then serves their common K/V; listing long groups first runs them first everywhere.
+  // A partial last query tile (Sq not a multiple of 256) has waves without rows, which
+  // only stage, and takes less time than a full one: an XCD runs the full tiles of all
+  // its units first and the partial ones after them (longest first), so the short ones
+  // fill the last round. The grid is padded to a multiple of 8 units.
   int qtile, bh, part;   // part: the partition, or for GROUPED the group
-  if constexpr (GROUPED) {
-    // Units (group, b, h) in the caller's group order are dealt round-robin over the 8
-    // XCDs (workgroup i runs on XCD i % 8); the query tiles of a unit run consecutively
-    // on one XCD, whose L2 then serves their common K/V. Listing long groups first runs
-    // them first everywhere. The grid is padded to a multiple of 8 units.
-    const int x = blockIdx.x % 8, s = blockIdx.x / 8;
-    const int j = x + 8 * (s / a.n_qtiles);
-    if (j >= a.G * a.B * a.H) return;
-    qtile = s % a.n_qtiles;
+  {
+    const int units = (GROUPED ? a.G : a.P) * a.B * a.H;
+    const int x = blockIdx.x % 8, s = blockIdx.x / 8, ux = (units + 7) / 8;
+    const int nf = a.Sq % kBQ ? a.n_qtiles - 1 : a.n_qtiles;   // full query tiles per unit
+    int k;
+    if (s < ux * nf) {
+      k = s / nf;
+      qtile = s - k * nf;
+    } else {
+      k = s - ux * nf;
+      qtile = a.n_qtiles - 1;
+    }
+    const int j = x + 8 * k;
+    if (j >= units) return;
     bh = j % (a.B * a.H);
     part = j / (a.B * a.H);
-  } else {
-    const int total = a.n_qtiles * a.B * a.H * a.P;
-    const int lid = xcd_remap(blockIdx.x, total);
-    qtile = lid % a.n_qtiles;
-    const int rest = lid / a.n_qtiles;
-    bh = rest % (a.B * a.H);
-    part = rest / (a.B * a.H);
   }
   const int b = bh / a.H, hh = bh % a.H;
 
@@ -1093,12 +1089,11 @@ hipError_t launch_variant(const AttnArgs& a, dim3 grid, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
-// Grid of a single-partition launch (query tiles x B*H x P), or of a grouped one: units
-// (group, b, h) padded to a multiple of 8 (the kernel's XCD mapping), times query tiles.
-// Zero blocks: nothing to launch; -1: too many.
+// Grid of a launch: units (partition, b, h), or (group, b, h) for a grouped one, padded to
+// a multiple of 8 (the kernel's XCD mapping), times query tiles. Zero blocks: nothing to
+// launch; -1: too many.
 inline int64_t attn_grid(const AttnArgs& a, bool grouped) {
-  const int64_t total = grouped ? ((int64_t)a.G * a.B * a.H + 7) / 8 * 8 * a.n_qtiles
-                                : (int64_t)a.n_qtiles * a.B * a.H * a.P;
+  const int64_t total = ((int64_t)(grouped ? a.G : a.P) * a.B * a.H + 7) / 8 * 8 * a.n_qtiles;
   return total > 0x7fffffff ? -1 : total;
 }
 
