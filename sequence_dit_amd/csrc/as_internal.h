@@ -40,6 +40,11 @@ struct AttnArgs {
   const float* v_scale;      // [B*H] (v_fp8 only)
   int64_t state_rows;        // B*H*Sq: rows of one partition's state
   int64_t payload_bytes;     // kOutFP8: bytes of one partition's state payload
+  int32_t split_kr;          // single-partition launches with partial query tiles: of the
+                             // C compute units of an XCD, split_kr run only partial tiles
+                             // and the others only full ones (0: full tiles first, then
+                             // partial ones); split_c = C. Set by the launch.
+  int32_t split_c;
   int32_t ranges[2 * AS_MAX_PARTITIONS];
   // Grouped launches (as_partition_attn_grouped): `ranges` holds the non-empty
   // partitions only, packed in group order (P of them); group g holds packed partitions

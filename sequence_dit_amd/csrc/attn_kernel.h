@@ -46,7 +46,10 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
+#include <functional>
+#include <vector>
 
 #include "as_internal.h"
 
@@ -685,16 +688,44 @@ void attn_bf16_kernel(const AttnArgs a) {
   // runs on XCD i % 8) and the query tiles of a unit run consecutively on its XCD, whose L2
   // then serves their common K/V; listing long groups first runs them first everywhere.
   // A partial last query tile (Sq not a multiple of 256) has waves without rows, which
-  // only stage, and takes less time than a full one: an XCD runs the full tiles of all
-  // its units first and the partial ones after them (longest first), so the short ones
-  // fill the last round. The grid is padded to a multiple of 8 units.
+  // only stage, and takes less time than a full one. An XCD runs the full tiles of all
+  // its units first and the partial ones after them (longest first), or, where the launch
+  // found it cheaper (split_kr > 0), in the order under which the hardware's in-order
+  // dispatch to free compute units keeps split_kr of them on partial tiles and the others
+  // on full ones: full tile f starts at 16 * floor(f / (C - split_kr)) and partial tile r
+  // at R16 * floor(r / split_kr) in units of a sixteenth of a full tile (R16 = 8 + the
+  // partial tile's waves with rows), and workgroups are issued in that order (full first
+  // on ties). The grid is padded to a multiple of 8 units.
   int qtile, bh, part;   // part: the partition, or for GROUPED the group
   {
     const int units = (GROUPED ? a.G : a.P) * a.B * a.H;
     const int x = blockIdx.x % 8, s = blockIdx.x / 8, ux = (units + 7) / 8;
     const int nf = a.Sq % kBQ ? a.n_qtiles - 1 : a.n_qtiles;   // full query tiles per unit
     int k;
-    if (s < ux * nf) {
+    if (!GROUPED && a.split_kr > 0) {
+      const int kr = a.split_kr, kf = a.split_c - kr;
+      const int NF = ux * nf, NR = ux * (a.n_qtiles - nf);
+      const int R16 = 8 + (a.Sq - nf * kBQ + kRowsPerWave - 1) / kRowsPerWave;
+      // position of full tile f in the issue order: f plus the partial tiles that start
+      // before it
+      auto pos_f = [&](int f) {
+        const int t = 16 * (f / kf);
+        return f + min(NR, kr * ((t + R16 - 1) / R16));
+      };
+      int lo = 0, hi = NF;   // g = number of full tiles at positions <= s
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (pos_f(mid) <= s) lo = mid + 1;
+        else hi = mid;
+      }
+      if (lo > 0 && pos_f(lo - 1) == s) {
+        k = (lo - 1) / nf;
+        qtile = lo - 1 - k * nf;
+      } else {
+        k = s - lo;
+        qtile = a.n_qtiles - 1;
+      }
+    } else if (s < ux * nf) {
       k = s / nf;
       qtile = s - k * nf;
     } else {
@@ -1068,15 +1099,75 @@ hipError_t launch_instance(const AttnArgs& a, dim3 grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Compute units of the current device (cached per device).
+inline int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+  }
+  return cus[dev];
+}
+
+// Issue order of a single-partition launch with partial query tiles (one workgroup per
+// compute unit: the kernel's registers allow no second). Costs in sixteenths of a full
+// tile: a full tile 16, a partial one R16. Longest first (full tiles, then partial ones)
+// leaves, per XCD of C compute units, about the load of the greedy assignment computed
+// below as `lpt`; keeping kr units on partial tiles and the others on full ones costs
+// max(16 ceil(NF / (C - kr)), R16 ceil(NR / kr)). The split with the least cost is taken
+// where it beats longest first (split_kr = kr), else split_kr = 0.
+inline void plan_issue_order(AttnArgs& a) {
+  a.split_kr = 0;
+  a.split_c = device_cus() / 8;
+  const int C = a.split_c;
+  const int nf = a.Sq % kBQ ? a.n_qtiles - 1 : a.n_qtiles;
+  const int64_t ux = ((int64_t)a.P * a.B * a.H + 7) / 8;
+  const int64_t NF = ux * nf, NR = ux * (a.n_qtiles - nf);
+  // long lists (many rounds) lose little to the last round: no planning
+  if (NR == 0 || NF == 0 || C < 2 || NF + NR > 4096) return;
+  const int64_t R16 = 8 + (a.Sq - nf * kBQ + kRowsPerWave - 1) / kRowsPerWave;
+  // the last plan, for repeated launches of one shape
+  thread_local int64_t key[4] = {-1, -1, -1, -1};
+  thread_local int kr_last = 0;
+  if (key[0] == NF && key[1] == NR && key[2] == R16 && key[3] == C) {
+    a.split_kr = kr_last;
+    return;
+  }
+  // greedy longest first: each tile to the least loaded unit (a min-heap of loads)
+  std::vector<int64_t> load(C, 0);
+  for (int64_t i = 0; i < NF + NR; ++i) {
+    std::pop_heap(load.begin(), load.end(), std::greater<int64_t>());
+    load.back() += i < NF ? 16 : R16;
+    std::push_heap(load.begin(), load.end(), std::greater<int64_t>());
+  }
+  int64_t best = *std::max_element(load.begin(), load.end());
+  for (int k = 1; k < C; ++k) {
+    const int64_t cost = std::max(16 * ((NF + C - k - 1) / (C - k)), R16 * ((NR + k - 1) / k));
+    if (cost < best) {
+      best = cost;
+      a.split_kr = k;
+    }
+  }
+  key[0] = NF;
+  key[1] = NR;
+  key[2] = R16;
+  key[3] = C;
+  kr_last = a.split_kr;
+}
+
 template <int D, bool QK8, bool GROUPED, bool V8>
 hipError_t launch_for_d(const AttnArgs& a, dim3 grid, hipStream_t stream) {
   if constexpr (GROUPED) {
     return launch_instance<D, kOutF32, QK8, true, V8>(a, grid, stream);
   } else {
-    switch (a.out_kind) {
-      case kOutF32: return launch_instance<D, kOutF32, QK8, false, V8>(a, grid, stream);
-      case kOutBF16: return launch_instance<D, kOutBF16, QK8, false, V8>(a, grid, stream);
-      case kOutFP8: return launch_instance<D, kOutFP8, QK8, false, V8>(a, grid, stream);
+    AttnArgs b = a;
+    plan_issue_order(b);
+    switch (b.out_kind) {
+      case kOutF32: return launch_instance<D, kOutF32, QK8, false, V8>(b, grid, stream);
+      case kOutBF16: return launch_instance<D, kOutBF16, QK8, false, V8>(b, grid, stream);
+      case kOutFP8: return launch_instance<D, kOutFP8, QK8, false, V8>(b, grid, stream);
       default: return hipErrorInvalidValue;
     }
   }
