@@ -126,13 +126,52 @@ def cpu_baseline(w, target_s, reuse):
 # GPU bench
 # --------------------------------------------------------------------------- #
 
+def _timed_launches(torch, launch, mode, scratch, reps):
+    """Launch time (ms) of `launch` in one of three modes. warm: inputs in the caches where
+    they fit; `reps` back-to-back launches between one event pair, averaged (events around
+    every launch would add their own gaps to a ~50 us kernel), median of 5 such batches.
+    cold: a read of a 512 MB scratch buffer before every launch, outside its events, so that
+    L2 and the 256 MB MALL hold none of the inputs; median of `reps` launches. cold_wflush:
+    the same with a 512 MB write instead, which also leaves up to 256 MB of dirty lines to
+    be written back while the launch runs."""
+    for _ in range(3):
+        launch()
+    if mode == "warm":
+        # no host synchronisation between batches: an idle GPU would start them at a lower clock
+        ev = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                launch()
+            b.record()
+            ev.append((a, b))
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) / reps for a, b in ev)
+        return ms[len(ms) // 2]
+    ev = []
+    sink = torch.zeros((), dtype=torch.float32, device=scratch.device)
+    for _ in range(reps):
+        if mode == "cold":
+            sink += scratch.sum()
+        else:
+            scratch.fill_(1.0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        launch()
+        b.record()
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    return ms[len(ms) // 2]
+
+
 def shape_sweep(N, inputs, torch, dev, reps=10):
-    """a1 alone on the image DiT and video DiT workloads, warm (back-to-back launches, inputs
-    and states in the 256 MB MALL where they fit) and cold (a 512 MB scratch write between
-    launches, outside the events). Median launch time; the fraction is max(t_MFMA, t_HBM) / t
-    with the algorithmic FLOP and bytes of the launch."""
+    """a1 alone on the image DiT and video DiT workloads, warm, cold and cold with a write flush
+    (`_timed_launches`). The fraction is max(t_MFMA, t_HBM) / t with the algorithmic FLOP and
+    bytes of the launch."""
     res = {}
-    scratch = torch.empty(512 << 18, dtype=torch.float32, device=dev)
+    scratch = torch.ones(512 << 18, dtype=torch.float32, device=dev)
     for cfg, name in ((2, "image"), (3, "video")):
         w = inputs.make(cfg)
         q, k, v = w.q.to(dev), w.k.to(dev), w.v.to(dev)
@@ -142,23 +181,13 @@ def shape_sweep(N, inputs, torch, dev, reps=10):
         flops = 4 * w.B * w.H * w.Sq * keys * w.D
         nbytes = 2 * w.B * w.H * (w.Sq * w.D + 2 * keys * w.D) + w.P * w.B * w.H * w.Sq * (4 * w.D + 4)
         t_floor = max(flops / (PEAK_BF16_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBPS * 1e9)) * 1e3
-        for mode in ("warm", "cold"):
-            for _ in range(3):
-                N.partition_attn(q, k, v, w.ranges, w.scale, out=out, lse=lse)
-            # no host synchronisation inside the loop: an idle GPU between launches would
-            # start the next one at a lower clock
-            ev = []
-            for _ in range(reps):
-                if mode == "cold":
-                    scratch.fill_(1.0)
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
-                N.partition_attn(q, k, v, w.ranges, w.scale, out=out, lse=lse)
-                b.record()
-                ev.append((a, b))
-            torch.cuda.synchronize()
-            ms = sorted(a.elapsed_time(b) for a, b in ev)
-            t = ms[len(ms) // 2]
+
+        # arguments checked and marshalled once: Python's per-call checks would outlast the
+        # ~50 us image launch and leave the GPU idle between back-to-back launches
+        launch, _, _ = N.prepare_partition_attn(q, k, v, w.ranges, w.scale, out=out, lse=lse)
+
+        for mode in ("warm", "cold", "cold_wflush"):
+            t = _timed_launches(torch, launch, mode, scratch, reps if mode != "warm" else (40 if cfg == 2 else 10))
             res[f"attn_{name}_{mode}"] = {"ms": round(t, 4), "TFLOP/s": round(flops / t / 1e9, 1),
                                           "frac_mfma": round(flops / t / 1e9 / PEAK_BF16_TFLOPS, 4),
                                           "frac_roofline": round(t_floor / t, 4)}
@@ -168,12 +197,12 @@ def shape_sweep(N, inputs, torch, dev, reps=10):
 
 
 def merge_sweep(N, torch, dev, state_out, state_lse, far, near_plus_cached, reps=10):
-    """as_merge alone, warm (back-to-back) and cold (a 512 MB scratch write before each launch, outside
-    its events, so the 256 MB MALL holds none of the inputs): the 32-way composition of all partition
-    states (the long-video workload's P-way merge), the 28-way composition of the far ones, and the
-    5-way merge of a reuse step. Median launch time; bytes = (k + 1) * rows * (4D + 4)."""
+    """as_merge alone, warm, cold and cold with a write flush (`_timed_launches`): the 32-way
+    composition of all partition states (the long-video workload's P-way merge), the 28-way
+    composition of the far ones, and the 5-way merge of a reuse step. Bytes = (k + 1) * rows *
+    (4D + 4)."""
     res = {}
-    scratch = torch.empty(512 << 18, dtype=torch.float32, device=dev)
+    scratch = torch.ones(512 << 18, dtype=torch.float32, device=dev)
     rows = state_lse[0].numel()
     D = state_out.shape[-1]
     out = torch.empty(state_out.shape[1:], dtype=torch.float32, device=dev)
@@ -184,21 +213,11 @@ def merge_sweep(N, torch, dev, state_out, state_lse, far, near_plus_cached, reps
     for name, idx, so, sl in cases:
         outs, lses = [so[i] for i in idx], [sl[i] for i in idx]
         by = (len(idx) + 1) * rows * (4 * D + 4)
-        for mode in ("warm", "cold"):
-            for _ in range(2):
-                N.merge(outs, lses, out=out, lse=lse)
-            ev = []
-            for _ in range(reps):
-                if mode == "cold":
-                    scratch.fill_(1.0)
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
-                N.merge(outs, lses, out=out, lse=lse)
-                b.record()
-                ev.append((a, b))
-            torch.cuda.synchronize()
-            ms = sorted(a.elapsed_time(b) for a, b in ev)
-            t = ms[len(ms) // 2]
+
+        launch, _, _ = N.prepare_merge(outs, lses, out=out, lse=lse)
+
+        for mode in ("warm", "cold", "cold_wflush"):
+            t = _timed_launches(torch, launch, mode, scratch, reps)
             res[f"{name}_{mode}"] = {"k": len(idx), "ms": round(t, 4), "GB/s": round(by / t / 1e6, 1),
                                      "frac_hbm": round(by / t / 1e6 / PEAK_HBM_GBPS, 4)}
     del scratch, out, lse

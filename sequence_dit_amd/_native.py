@@ -347,6 +347,28 @@ def _state_outputs(q, P, B, H, Sq, D, state_dtype, out, lse):
 
 
 def _attn(q, k, v, kv_ranges, scale, out, lse, state_dtype):
+    fn, args, out, lse = _attn_call(q, k, v, kv_ranges, scale, out, lse, state_dtype)
+    check(fn(*args))
+    return out, lse
+
+
+def prepare_partition_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_ranges: Sequence[Tuple[int, int]],
+                           scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                           lse: Optional[torch.Tensor] = None):
+    """partition_attn with its arguments checked and marshalled once: returns (launch, out, lse),
+    where launch() enqueues the same as_partition_attn call on the stream current now. For
+    repeated launches of one shape (timing short launches, whose per-call checks in Python
+    would otherwise outlast them)."""
+    fn, args, out, lse = _attn_call(q, k, v, kv_ranges, scale, out, lse, None)
+
+    def launch() -> None:
+        check(fn(*args))
+
+    return launch, out, lse
+
+
+def _attn_call(q, k, v, kv_ranges, scale, out, lse, state_dtype):
+    """(C function, its arguments, out, lse) of a single-partition launch, checked."""
     if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or k.stride() != v.stride():
         raise ValueError("q must be [B,H,Sq,D]; k and v [B,H,Skv,D] with equal strides")
     if q.dtype != k.dtype or k.dtype != v.dtype or q.dtype not in (torch.bfloat16, torch.float32):
@@ -369,10 +391,9 @@ def _attn(q, k, v, kv_ranges, scale, out, lse, state_dtype):
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), dt, B, H, Sq, Skv, D,
             _i64(q.stride()[:3]), _i64(k.stride()[:3]), ranges, P, sc)
     if state_dtype is None:
-        check(lib().as_partition_attn(*args, out.data_ptr(), lse.data_ptr(), _stream(q)))
-    else:
-        check(lib().as_partition_attn_states(*args, code, _out_tensor(out).data_ptr(), lse.data_ptr(), _stream(q)))
-    return out, lse
+        return lib().as_partition_attn, args + (out.data_ptr(), lse.data_ptr(), _stream(q)), out, lse
+    return (lib().as_partition_attn_states, args + (code, _out_tensor(out).data_ptr(), lse.data_ptr(), _stream(q)),
+            out, lse)
 
 
 def partition_attn_grouped(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_ranges: Sequence[Tuple[int, int]],
@@ -448,6 +469,25 @@ def partition_attn_grouped(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv
 def merge(outs: Sequence[torch.Tensor], lses: Sequence[torch.Tensor], out: Optional[torch.Tensor] = None,
           lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Compose n states (OUT_k [..., D], LSE_k [...]) into one; returns (OUT, LSE)."""
+    fn, args, out, lse = _merge_call(outs, lses, out, lse)
+    check(fn(*args))
+    return out, lse
+
+
+def prepare_merge(outs: Sequence[torch.Tensor], lses: Sequence[torch.Tensor], out: Optional[torch.Tensor] = None,
+                  lse: Optional[torch.Tensor] = None):
+    """merge with its arguments checked and marshalled once: returns (launch, out, lse), where
+    launch() enqueues the same as_merge call on the stream current now."""
+    fn, args, out, lse = _merge_call(outs, lses, out, lse)
+
+    def launch() -> None:
+        check(fn(*args))
+
+    return launch, out, lse
+
+
+def _merge_call(outs, lses, out, lse):
+    """(C function, its arguments, out, lse) of as_merge, checked."""
     n = len(outs)
     if n != len(lses) or n == 0:
         raise ValueError("need the same positive number of OUT and LSE tensors")
@@ -465,8 +505,7 @@ def merge(outs: Sequence[torch.Tensor], lses: Sequence[torch.Tensor], out: Optio
     _require_gpu(*outs, *lses, out, lse)
     optrs = (ctypes.c_void_p * n)(*[o.data_ptr() for o in outs])
     lptrs = (ctypes.c_void_p * n)(*[l.data_ptr() for l in lses])
-    check(lib().as_merge(n, optrs, lptrs, rows, D, out.data_ptr(), lse.data_ptr(), _stream(outs[0])))
-    return out, lse
+    return lib().as_merge, (n, optrs, lptrs, rows, D, out.data_ptr(), lse.data_ptr(), _stream(outs[0])), out, lse
 
 
 def _state_list(outs) -> Tuple[torch.dtype, int, int, Tuple[int, ...], List[int]]:

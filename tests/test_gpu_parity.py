@@ -827,3 +827,23 @@ def test_full_size_grouped_selective_reuse(reuse_workload, reuse_reference, near
     assert np.abs(got - l_t[order]).max() <= BF16_LSE
     got1 = runner.step_lse[:len(w.near), :, heads].cpu().double().numpy()
     assert np.abs(got1 - l_t1[w.near]).max() <= BF16_LSE
+
+
+def test_prepared_launches_repeat_the_plain_calls_bitwise():
+    """prepare_partition_attn / prepare_merge: arguments marshalled once, the same C calls; every
+    repeated launch gives the plain call's result bit for bit."""
+    w = inputs.small_case(31, 1, 2, 300, 1000, 128, RAGGED)
+    q, k, v = to_dev(w.q), to_dev(w.k), to_dev(w.v)
+    note("prepared launches: partition_attn D=128 B=1 H=2 Sq=300 P=7, then a 7-way merge")
+    out, lse = N.partition_attn(q, k, v, w.ranges, w.scale)
+    launch, p_out, p_lse = N.prepare_partition_attn(q, k, v, w.ranges, w.scale)
+    m_out, m_lse = N.merge(list(out), list(lse))
+    mlaunch, pm_out, pm_lse = N.prepare_merge(list(out), list(lse))
+    for _ in range(3):
+        p_out.zero_()
+        pm_out.zero_()
+        launch()
+        mlaunch()
+        torch.cuda.synchronize()
+        assert torch.equal(p_out, out) and torch.equal(p_lse, lse)
+        assert torch.equal(pm_out, m_out) and torch.equal(pm_lse, m_lse)
