@@ -53,76 +53,81 @@ def lib() -> ctypes.CDLL:
     """Load the library (once); raises if it has not been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"HIP library {LIB_PATH} is missing: build it with "
-                               "`python -m sequence_dit_amd.build` (or __graft_entry__.build())")
-        L = ctypes.CDLL(LIB_PATH)
-        L.as_partition_attn.restype = ctypes.c_int
-        L.as_partition_attn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
-                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
-                                        c_i64p, c_i64p, c_i32p, ctypes.c_int32, ctypes.c_float,
-                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
-        L.as_merge.restype = ctypes.c_int
-        L.as_merge.argtypes = [ctypes.c_int32, c_vpp, c_vpp, ctypes.c_int64, ctypes.c_int64,
-                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
-        L.as_partition_attn_states.restype = ctypes.c_int
-        L.as_partition_attn_states.argtypes = L.as_partition_attn.argtypes[:14] + [ctypes.c_int, ctypes.c_void_p,
-                                                                                   ctypes.c_void_p, ctypes.c_void_p]
-        L.as_partition_attn_fp8.restype = ctypes.c_int
-        L.as_partition_attn_fp8.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                                            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
-                                            ctypes.c_int64, ctypes.c_int64, c_i64p, c_i64p, c_i32p, ctypes.c_int32,
-                                            ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
-                                            ctypes.c_void_p]
-        L.as_partition_attn_fp8_qkv.restype = ctypes.c_int
-        L.as_partition_attn_fp8_qkv.argtypes = (L.as_partition_attn_fp8.argtypes[:5] + [ctypes.c_void_p]
-                                                + L.as_partition_attn_fp8.argtypes[5:])
-        L.as_state_bytes.restype = ctypes.c_size_t
-        L.as_state_bytes.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64]
-        L.as_partition_attn_grouped.restype = ctypes.c_int
-        L.as_partition_attn_grouped.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
-                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                                                ctypes.c_int64, ctypes.c_int64,
-                                                ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, c_i64p, c_i64p, c_i32p,
-                                                ctypes.c_int32, c_i32p, ctypes.c_int32, ctypes.c_float,
-                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                                                ctypes.c_void_p, ctypes.c_void_p]
-        L.as_merge_states.restype = ctypes.c_int
-        L.as_merge_states.argtypes = [ctypes.c_int32, c_vpp, c_vpp, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
-                                      ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
-        L.as_compose_groups.restype = ctypes.c_int
-        L.as_compose_groups.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int32, ctypes.c_int64,
-                                        ctypes.c_int64, ctypes.c_int32, ctypes.c_int, ctypes.c_void_p,
-                                        ctypes.c_void_p, ctypes.c_void_p]
-        L.as_partition_contribution_workspace_size.restype = ctypes.c_size_t
-        L.as_partition_contribution_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int64]
-        L.as_partition_contribution.restype = ctypes.c_int
-        L.as_partition_contribution.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
-                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
-                                                ctypes.c_void_p]
-        L.as_partition_contribution_noalloc.restype = ctypes.c_int
-        L.as_partition_contribution_noalloc.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
-                                                        ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
-                                                        ctypes.c_void_p]
-        L.as_state_norms_workspace_size.restype = ctypes.c_size_t
-        L.as_state_norms_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int64]
-        L.as_state_norms.restype = ctypes.c_int
-        L.as_state_norms.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
-                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
-        L.as_planner_decide.restype = ctypes.c_int
-        L.as_planner_decide.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
-                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                                        ctypes.c_void_p, ctypes.c_void_p]
-        L.as_planner_epsilon.restype = ctypes.c_int
-        L.as_planner_epsilon.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
-                                         ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
-        L.as_status_string.restype = ctypes.c_char_p
-        L.as_status_string.argtypes = [ctypes.c_int]
-        L.as_last_error.restype = ctypes.c_char_p
-        L.as_last_error.argtypes = []
-        _lib = L
+        _lib = load(LIB_PATH)
     return _lib
+
+
+def load(path: str) -> ctypes.CDLL:
+    """Open a build of the library at `path` with the C signatures declared."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library {path} is missing: build it with "
+                           "`python -m sequence_dit_amd.build` (or __graft_entry__.build())")
+    L = ctypes.CDLL(path)
+    L.as_partition_attn.restype = ctypes.c_int
+    L.as_partition_attn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                    ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                    c_i64p, c_i64p, c_i32p, ctypes.c_int32, ctypes.c_float,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    L.as_merge.restype = ctypes.c_int
+    L.as_merge.argtypes = [ctypes.c_int32, c_vpp, c_vpp, ctypes.c_int64, ctypes.c_int64,
+                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    L.as_partition_attn_states.restype = ctypes.c_int
+    L.as_partition_attn_states.argtypes = L.as_partition_attn.argtypes[:14] + [ctypes.c_int, ctypes.c_void_p,
+                                                                               ctypes.c_void_p, ctypes.c_void_p]
+    L.as_partition_attn_fp8.restype = ctypes.c_int
+    L.as_partition_attn_fp8.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.c_int64, ctypes.c_int64, c_i64p, c_i64p, c_i32p, ctypes.c_int32,
+                                        ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    L.as_partition_attn_fp8_qkv.restype = ctypes.c_int
+    L.as_partition_attn_fp8_qkv.argtypes = (L.as_partition_attn_fp8.argtypes[:5] + [ctypes.c_void_p]
+                                            + L.as_partition_attn_fp8.argtypes[5:])
+    L.as_state_bytes.restype = ctypes.c_size_t
+    L.as_state_bytes.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64]
+    L.as_partition_attn_grouped.restype = ctypes.c_int
+    L.as_partition_attn_grouped.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_int64, ctypes.c_int64,
+                                            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, c_i64p, c_i64p, c_i32p,
+                                            ctypes.c_int32, c_i32p, ctypes.c_int32, ctypes.c_float,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_void_p]
+    L.as_merge_states.restype = ctypes.c_int
+    L.as_merge_states.argtypes = [ctypes.c_int32, c_vpp, c_vpp, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    L.as_compose_groups.restype = ctypes.c_int
+    L.as_compose_groups.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int32, ctypes.c_int64,
+                                    ctypes.c_int64, ctypes.c_int32, ctypes.c_int, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p]
+    L.as_partition_contribution_workspace_size.restype = ctypes.c_size_t
+    L.as_partition_contribution_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int64]
+    L.as_partition_contribution.restype = ctypes.c_int
+    L.as_partition_contribution.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                            ctypes.c_void_p]
+    L.as_partition_contribution_noalloc.restype = ctypes.c_int
+    L.as_partition_contribution_noalloc.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                                    ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                                    ctypes.c_void_p]
+    L.as_state_norms_workspace_size.restype = ctypes.c_size_t
+    L.as_state_norms_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int64]
+    L.as_state_norms.restype = ctypes.c_int
+    L.as_state_norms.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    L.as_planner_decide.restype = ctypes.c_int
+    L.as_planner_decide.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p]
+    L.as_planner_epsilon.restype = ctypes.c_int
+    L.as_planner_epsilon.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
+    L.as_status_string.restype = ctypes.c_char_p
+    L.as_status_string.argtypes = [ctypes.c_int]
+    L.as_last_error.restype = ctypes.c_char_p
+    L.as_last_error.argtypes = []
+    return L
 
 
 def check(status: int) -> None:

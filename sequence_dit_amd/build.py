@@ -19,6 +19,10 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libas_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+# Diagnostics library: the same, with the single-partition bf16 kernels built with
+# -DAS_WG_STAMPS (per-workgroup timestamps; see sequence_dit_amd/wg_stamps.py).
+STAMPS_LIB_PATH = os.path.join(PKG, "libas_attn_stamps.so")
+STAMPS_SOURCE = "partition_attn.hip"
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "partition_attn.hip", "partition_attn_fp8.hip", "partition_attn_fp8v.hip", "partition_attn_grouped.hip", "merge.hip",
@@ -68,11 +72,17 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         objs.append(obj)
         cmds.append([cc, *COMMON_FLAGS, *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
                      "-o", obj])
+    stamps_obj = os.path.join(BUILD_DIR, STAMPS_SOURCE.replace(".hip", "_stamps.o"))
+    cmds.append([cc, *COMMON_FLAGS, *DEVICE_FLAGS, *SOURCE_FLAGS.get(STAMPS_SOURCE, []), "-DAS_WG_STAMPS", "-c",
+                 os.path.join(CSRC, STAMPS_SOURCE), "-o", stamps_obj])
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as pool:
         list(pool.map(lambda c: _run(c, verbose), cmds))
-    tmp = LIB_PATH + ".tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB_PATH)
+    for path, objects in ((LIB_PATH, objs),
+                          (STAMPS_LIB_PATH, [stamps_obj if os.path.basename(o) == STAMPS_SOURCE.replace(".hip", ".o")
+                                             else o for o in objs])):
+        tmp = path + ".tmp"
+        _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objects], verbose)
+        os.replace(tmp, path)
     return LIB_PATH
 
 

@@ -91,6 +91,24 @@ __device__ __forceinline__ unsigned fp8x4(float a, float b, float c, float d) {
 }
 __device__ __forceinline__ float clamp448(float x) { return fminf(fmaxf(x, -448.0f), 448.0f); }
 
+#ifdef AS_WG_STAMPS
+// Diagnostics build only (compiled with -DAS_WG_STAMPS into libas_attn_stamps.so, never into
+// the product library): workgroup i < kStampWGs of a single-partition launch records, from
+// its first thread, 8 words: s_memrealtime (100 MHz) at its start, after its first barrier
+// (K tile 0 in LDS), after its last tile and at its end; s_memtime (shader clock) at its
+// start and end; its query tile and partition; its HW_ID and XCC_ID registers.
+constexpr int kStampWGs = 16384;
+__device__ unsigned long long as_wg_stamps[kStampWGs * 8];
+#define AS_STAMP(i, value)                                                                     \
+  do {                                                                                         \
+    if (threadIdx.x == 0 && blockIdx.x < kStampWGs) as_wg_stamps[8 * blockIdx.x + (i)] = (value); \
+  } while (0)
+#else
+#define AS_STAMP(i, value) \
+  do {                     \
+  } while (0)
+#endif
+
 constexpr int kWaves = 8;
 constexpr int kQB = 1;                       // 32-row query blocks per wave
 constexpr int kRowsPerWave = 32 * kQB;       // 32
@@ -738,6 +756,12 @@ void attn_bf16_kernel(const AttnArgs a) {
     part = j / (a.B * a.H);
   }
   const int b = bh / a.H, hh = bh % a.H;
+  if constexpr (!GROUPED) {
+    AS_STAMP(0, __builtin_amdgcn_s_memrealtime());
+    AS_STAMP(4, __builtin_amdgcn_s_memtime());
+    AS_STAMP(6, (unsigned long long)qtile | ((unsigned long long)part << 32));
+    AS_STAMP(7, __builtin_amdgcn_s_getreg((31 << 11) | 4) | ((unsigned long long)__builtin_amdgcn_s_getreg((31 << 11) | 20) << 32));
+  }
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -957,6 +981,7 @@ void attn_bf16_kernel(const AttnArgs a) {
     } else {
       LDV(0);
       lds_barrier();
+      if constexpr (!GROUPED) AS_STAMP(1, __builtin_amdgcn_s_memrealtime());
       if constexpr (ON) w.template mfma_phase<0, 0, true, false>(smem);  // X_0
       lds_barrier();
       if constexpr (ON) SMX(0, std::true_type{});                    // Y_0
@@ -1043,6 +1068,7 @@ void attn_bf16_kernel(const AttnArgs a) {
     start_partition(ks, n);
     if (__builtin_amdgcn_readfirstlane(q0 + wave * kRowsPerWave) < a.Sq) schedule(std::true_type{});
     else schedule(std::false_type{});
+    AS_STAMP(2, __builtin_amdgcn_s_memrealtime());
 
     // ---- epilogue: OUT = O / l, LSE = (m + log2 l) ln 2
     const float lt = wave_sum_halves(w.l);
@@ -1089,6 +1115,13 @@ void attn_bf16_kernel(const AttnArgs a) {
       if (half == 0 && qrow < a.Sq) lse[qrow] = (w.m + __log2f(lt)) * 0.69314718055994530942f;
     }
   }
+#ifdef AS_WG_STAMPS
+  if constexpr (!GROUPED) {
+    __syncthreads();
+    AS_STAMP(3, __builtin_amdgcn_s_memrealtime());
+    AS_STAMP(5, __builtin_amdgcn_s_memtime());
+  }
+#endif
 }
 
 // Launch of one instance: D from the arguments, OUT from a.out_kind (single-partition

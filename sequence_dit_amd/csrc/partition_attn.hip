@@ -134,3 +134,16 @@ hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream) {
 }
 
 }  // namespace as
+
+#ifdef AS_WG_STAMPS
+// Diagnostics build only: copies (or clears) the workgroup stamps of the single-partition
+// bf16 kernels of this file; returns a hipError_t.
+extern "C" int as_debug_wg_stamps(void* host, size_t bytes) {
+  if (bytes > sizeof(as::as_wg_stamps)) bytes = sizeof(as::as_wg_stamps);
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(as::as_wg_stamps), bytes);
+}
+extern "C" int as_debug_wg_stamps_clear() {
+  static unsigned long long zeros[as::kStampWGs * 8];
+  return (int)hipMemcpyToSymbol(HIP_SYMBOL(as::as_wg_stamps), zeros, sizeof(zeros));
+}
+#endif

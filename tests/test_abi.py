@@ -28,6 +28,18 @@ def test_exports_every_declared_symbol():
         assert hasattr(L, name), name
 
 
+def test_diagnostics_build_is_separate():
+    """The workgroup-stamp entry points exist only in the diagnostics library, which exports
+    the same declared C ABI besides them."""
+    from sequence_dit_amd import build, wg_stamps
+    assert not hasattr(ctypes.CDLL(N.LIB_PATH), "as_debug_wg_stamps")
+    if not os.path.exists(build.STAMPS_LIB_PATH):
+        pytest.skip("diagnostics library not built")
+    L = wg_stamps._load()
+    for name in N.EXPORTS:
+        getattr(L, name)
+
+
 def test_status_strings():
     L = N.lib()
     assert L.as_status_string(N.AS_OK) == b"ok"
