@@ -35,6 +35,17 @@ ATTN_SOURCES = [os.path.join(ROOT, "sequence_dit_amd", "csrc", f)
                 for f in ("attn_kernel.h", "partition_attn.hip", "partition_attn_grouped.hip")]
 # the anchor composes the far partitions in runs of this many inside the attention launch
 FAR_GROUP = 4
+# The next step's near partitions, two per grouped launch: the cached state is folded into
+# the first group's result and the two group states are composed by a 2-way merge (measured
+# faster than one launch per near partition plus a 5-way merge, and than one group of four)
+NEAR_GROUP = 2
+
+
+def reuse_step(runner, anchor_in, step_in, anchor_scales=None, step_scales=None):
+    """One selective-reuse step as bench.py times it: the grouped anchor, then the next step's
+    near partitions in groups of NEAR_GROUP."""
+    runner.anchor_grouped(*anchor_in, FAR_GROUP, anchor_scales)
+    return runner.step_grouped(*step_in, NEAR_GROUP, step_scales)
 
 
 def log(msg):
@@ -227,16 +238,15 @@ def merge_sweep(N, torch, dev, state_out, state_lse, far, near_plus_cached, reps
 def variant_sweep(runner, torch, q, k, v, q1, k1, v1, steps, ms_step, step_flops, attn_flops):
     """The reuse step in other arrangements of the same work, each timed as a whole step like the
     main one and per call: every launch ungrouped (the anchor writes all 32 partition states, then
-    the 28-way composition of the far ones), and grouped launches at the next step too (the cached
-    state folded into the near partitions' composed state in one launch, or in two groups plus a
-    3-way merge)."""
+    the 28-way composition of the far ones; one launch for the near partitions and a 5-way merge
+    at the next step), the grouped anchor with that ungrouped next step, and the grouped anchor
+    with all near partitions in one group (the cached state folded in, no merge)."""
     res = {}
     anchor_flops = attn_flops["attn_anchor_grouped"]
     variants = (("ungrouped", lambda: (runner.anchor(q, k, v), runner.step(q1, k1, v1))),
-                ("grouped_both", lambda: (runner.anchor_grouped(q, k, v, FAR_GROUP),
-                                          runner.step_grouped(q1, k1, v1, None))),
-                ("grouped_both_near2", lambda: (runner.anchor_grouped(q, k, v, FAR_GROUP),
-                                                runner.step_grouped(q1, k1, v1, 2))))
+                ("grouped_anchor_only", lambda: (runner.anchor_grouped(q, k, v, FAR_GROUP), runner.step(q1, k1, v1))),
+                ("grouped_near_in_one", lambda: (runner.anchor_grouped(q, k, v, FAR_GROUP),
+                                                 runner.step_grouped(q1, k1, v1, None))))
     for tag, fn in variants:
         runner.timer = None
         fn()
@@ -260,8 +270,8 @@ def variant_sweep(runner, torch, q, k, v, q1, k1, v1, steps, ms_step, step_flops
         for name, ts in times.items():
             ms = sum(ts) / len(ts)
             entry = {"ms": round(ms, 4)}
-            fl = {"attn_anchor": anchor_flops, "attn_anchor_grouped": anchor_flops, "attn_fresh": attn_flops["attn_fresh"],
-                  "attn_fresh_grouped": attn_flops["attn_fresh"]}.get(name)
+            fl = {"attn_anchor": anchor_flops, "attn_anchor_grouped": anchor_flops,
+                  "attn_fresh": attn_flops["attn_fresh_grouped"], "attn_fresh_grouped": attn_flops["attn_fresh_grouped"]}.get(name)
             if fl:
                 entry["TFLOP/s"] = round(fl / ms / 1e9, 1)
                 entry["frac_mfma"] = round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4)
@@ -317,8 +327,7 @@ def main():
 
     def step():
         if reuse:
-            runner.anchor_grouped(q, k, v, FAR_GROUP)
-            runner.step(q1, k1, v1)
+            reuse_step(runner, (q, k, v), (q1, k1, v1))
         else:
             runner._timed("attn_anchor", N.partition_attn, q, k, v, w.ranges, w.scale,
                           out=runner.state_out, lse=runner.state_lse)
@@ -338,7 +347,11 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    runner.timer = []
+    # the dominant kernel: the anchor's attention launch (grouped for the reuse workload); inside
+    # the timed region only its launches are bracketed by events (every event pair on the
+    # stream costs the step a few microseconds)
+    dom = "attn_anchor_grouped" if reuse else "attn_anchor"
+    runner.timer, runner.timer_only = [], {dom}
     log(f"timing {args.steps} steps")
     t0 = time.perf_counter()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -350,10 +363,17 @@ def main():
     wall_ms = (time.perf_counter() - t0) * 1e3
     ms_step = start.elapsed_time(end) / args.steps
     log(f"timed region: {ms_step:.3f} ms/step (wall {wall_ms / args.steps:.3f} ms/step)")
+    dom_times = [s.elapsed_time(e) for name, s, e in runner.timer]
 
+    # every launch of the step timed on its own, in further steps after the timed region
+    runner.timer, runner.timer_only = [], None
+    for _ in range(max(2, args.steps // 2)):
+        step()
+    torch.cuda.synchronize()
     times = {}
     for name, s, e in runner.timer:
         times.setdefault(name, []).append(s.elapsed_time(e))
+    runner.timer = None
     rows = w.B * w.H * w.Sq
     state_bytes = rows * (4 * w.D + 4)
     per_key = 4 * w.B * w.H * w.Sq * w.D
@@ -375,18 +395,20 @@ def main():
         attn_bytes["attn_anchor_grouped"] = (2 * w.B * w.H * (w.Sq * w.D + 2 * all_keys * w.D) + n_groups * state_bytes
                                              + w.P * rows * 4)
         fresh_keys = sum(w.ranges[i][1] - w.ranges[i][0] for i in near)
-        attn_flops["attn_fresh"] = per_key * fresh_keys
-        attn_bytes["attn_fresh"] = 2 * w.B * w.H * (w.Sq * w.D + 2 * fresh_keys * w.D) + len(near) * state_bytes
-        merges = {"merge_cached_grouped": n_far_groups, "merge_step": len(near) + 1}
+        n_near_groups = (len(near) + NEAR_GROUP - 1) // NEAR_GROUP
+        attn_flops["attn_fresh_grouped"] = per_key * fresh_keys
+        # Q and the near partitions' K/V, the cached state folded in, the group states and
+        # every near partition's LSE
+        attn_bytes["attn_fresh_grouped"] = (2 * w.B * w.H * (w.Sq * w.D + 2 * fresh_keys * w.D)
+                                            + (1 + n_near_groups) * state_bytes + len(near) * rows * 4)
+        merges = {"merge_cached_grouped": n_far_groups, "merge_step_grouped": n_near_groups}
         contribs["contrib_step"] = len(near) + 1
     else:
         merges = {"merge_all": w.P}
 
     step_flops = sum(attn_flops.values())
-    # the dominant kernel: the anchor's attention launch (grouped for the reuse workload)
-    dom = "attn_anchor_grouped" if reuse else "attn_anchor"
-    attn_ms = sum(times[dom])
-    attn_launches = len(times[dom])
+    attn_ms = sum(dom_times)
+    attn_launches = len(dom_times)
     attn_total_flops = attn_flops[dom] * attn_launches
     achieved = attn_total_flops / (attn_ms * 1e-3) / 1e12
     kernels = {}
@@ -429,7 +451,7 @@ def main():
         e2.record()
         torch.cuda.synchronize()
         near_mass = runner.anchor_scores[:, near].sum(dim=1).mean().item()
-        fresh_ms = kernels["attn_fresh"]["ms"] + kernels["merge_step"]["ms"]
+        fresh_ms = kernels["attn_fresh_grouped"]["ms"] + kernels["merge_step_grouped"]["ms"]
         reuse_quality = {
             "mse_vs_full": float(torch.mean((r_out - f_out) ** 2).item()),
             "lse_max_abs_vs_full": float((r_lse - f_lse).abs().max().item()),
@@ -547,27 +569,23 @@ def main():
 
         # the whole step (anchor + next step, with their compositions and weights) on fp8 q/k
         runner.timer = None
-        runner.anchor_grouped(q8, k8, v, FAR_GROUP, (qs8, ks8))
-        runner.step(q18, k18, v1, (qs18, ks18))
+        reuse_step(runner, (q8, k8, v), (q18, k18, v1), (qs8, ks8), (qs18, ks18))
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(args.steps):
-            runner.anchor_grouped(q8, k8, v, FAR_GROUP, (qs8, ks8))
-            runner.step(q18, k18, v1, (qs18, ks18))
+            reuse_step(runner, (q8, k8, v), (q18, k18, v1), (qs8, ks8), (qs18, ks18))
         e1.record()
         torch.cuda.synchronize()
         fp8_step_ms = e0.elapsed_time(e1) / args.steps
         kernels["step_fp8"] = {"ms": round(fp8_step_ms, 4), "TFLOP/s": round(step_flops / fp8_step_ms / 1e9, 1),
                                "speedup_vs_bf16": round(ms_step / fp8_step_ms, 3)}
         # and on fp8 q/k/v
-        runner.anchor_grouped(q8, k8, v8, FAR_GROUP, (qs8, ks8, vs8))
-        runner.step(q18, k18, v18, (qs18, ks18, vs18))
+        reuse_step(runner, (q8, k8, v8), (q18, k18, v18), (qs8, ks8, vs8), (qs18, ks18, vs18))
         torch.cuda.synchronize()
         e0.record()
         for _ in range(args.steps):
-            runner.anchor_grouped(q8, k8, v8, FAR_GROUP, (qs8, ks8, vs8))
-            runner.step(q18, k18, v18, (qs18, ks18, vs18))
+            reuse_step(runner, (q8, k8, v8), (q18, k18, v18), (qs8, ks8, vs8), (qs18, ks18, vs18))
         e1.record()
         torch.cuda.synchronize()
         ms8 = e0.elapsed_time(e1) / args.steps
@@ -585,9 +603,9 @@ def main():
         for name, s, e in runner.timer:
             ftimes.setdefault(name, []).append(s.elapsed_time(e))
         for name, base, fl in (("attn_anchor_fp8", "attn_anchor_bf16", anchor_flops),
-                               ("attn_fresh_fp8", "attn_fresh_bf16", attn_flops["attn_fresh"]),
+                               ("attn_fresh_fp8", "attn_fresh_bf16", attn_flops["attn_fresh_grouped"]),
                                ("attn_anchor_fp8qkv", "attn_anchor_bf16", anchor_flops),
-                               ("attn_fresh_fp8qkv", "attn_fresh_bf16", attn_flops["attn_fresh"])):
+                               ("attn_fresh_fp8qkv", "attn_fresh_bf16", attn_flops["attn_fresh_grouped"])):
             ms = sum(ftimes[name]) / len(ftimes[name])
             ms16 = sum(ftimes[base]) / len(ftimes[base])
             tf = fl / ms / 1e9
@@ -606,7 +624,7 @@ def main():
                 "avg_launch_ms": round(attn_ms / attn_launches, 4)}
 
     if reuse and not args.main_only:
-        log("the step with every launch ungrouped, and with grouped launches at both steps")
+        log("other arrangements of the step")
         kernels.update(variant_sweep(runner, torch, q, k, v, q1, k1, v1, args.steps, ms_step, step_flops,
                                      attn_flops))
         log("merges warm and cold (32-way, 28-way, 5-way)")

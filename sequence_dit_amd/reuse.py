@@ -36,7 +36,9 @@ class SelectiveReuse:
     def __init__(self, B: int, H: int, Sq: int, D: int, ranges: Sequence[Tuple[int, int]], near: Sequence[int],
                  device, scale: float | None = None):
         # optional list that receives (name, start_event, end_event) around every library call
+        # (or, with timer_only set, around the calls of those names only)
         self.timer: List | None = None
+        self.timer_only: set | None = None
         self.ranges = [tuple(r) for r in ranges]
         self.P = len(self.ranges)
         self.near = sorted(int(i) for i in near)
@@ -84,7 +86,7 @@ class SelectiveReuse:
         return self.step_lse[-1]
 
     def _timed(self, name: str, fn, *args, **kw):
-        if self.timer is None:
+        if self.timer is None or (self.timer_only is not None and name not in self.timer_only):
             return fn(*args, **kw)
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         start.record()
