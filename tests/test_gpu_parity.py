@@ -111,7 +111,7 @@ FP8_BLOCK, FP8_ALIGN_BITS = 64, 16
 def fp8_score_bound(qd, kd, ranges, scale):
     """Per-element bound [P, B, H, Sq] on |LSE - LSE_exact| for fp8 q/k (decoded values qd, kd):
     the truncation model above for each score, the largest over the range (LSE is a smooth
-    maximum), |scale| times, plus the benchmark spec's 1e-3."""
+    maximum), |scale| times, plus the 1e-3 LSE tolerance of bf16 inputs."""
     qa = np.abs(np.asarray(qd, dtype=np.float64))
     ka = np.abs(np.asarray(kd, dtype=np.float64))
     D = qa.shape[-1]
@@ -133,7 +133,7 @@ def score_rounding_bound(q, k, ranges, scale, unit=2.0 ** -24):
     is off by at most D * 2^-24 * sum_d |q_d k_d| (the gamma_D bound of floating-point
     summation, to first order), so each scaled score by that times |scale|. LSE is a smooth
     maximum of the scores, so it moves by at most the largest score error over the range. The
-    the benchmark spec's 1e-3 is added for the softmax, exponential and log."""
+    1e-3 LSE tolerance of bf16 inputs is added for the softmax, exponential and log."""
     qa = np.abs(np.asarray(q, dtype=np.float64))
     ka = np.abs(np.asarray(k, dtype=np.float64))
     D = qa.shape[-1]
@@ -159,7 +159,7 @@ def check_lse_within(lse, l_ref, bound, what):
 def test_bf16_large_logits_stay_finite(D):
     """Scores scaled x100 (very peaked softmax, many lazy rescales, |LSE| up to ~300): no overflow,
     NaN, or loss of parity; the 17-key partition exercises the tail mask at both tile sizes. LSE is
-    held to the benchmark spec's 1e-3 (a rescale slip that lost a percent of a partition's mass would
+    held to the 1e-3 LSE tolerance of bf16 inputs (a rescale slip that lost a percent of a partition's mass would
     move it by 1e-2); the fp32 score-accumulation bound of these inputs (score_rounding_bound, a few
     1e-3) is larger, and the errors measured on the GPU are below 1e-4."""
     w = inputs.small_case(31 if D == 128 else 95, 1, 2, 64, 500, D, [(0, 500), (0, 17), (250, 500)])
