@@ -71,6 +71,23 @@ def test_bf16_small_ragged(D):
     check_states(out, lse, o_ref, l_ref, BF16_OUT, BF16_LSE, f"bf16 D={D}")
 
 
+SPLIT_RANGES = [(0, 400), (400, 400), (400, 401), (401, 1200), (1200, 1333), (1333, 2100), (2100, 3000), (0, 3000)]
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_partial_tiles_issued_on_their_own_compute_units(D):
+    """22 heads x 8 partitions x 520 query rows: two full query tiles and an 8-row one per
+    unit, a shape whose launch keeps part of each XCD's compute units on the partial tiles
+    (the issue order changes; every tile must still be computed once). Every element against
+    the oracle; ragged, empty, single-key and overlapping ranges."""
+    w = inputs.small_case(61 + D, 1, 22, 520, 3000, D, SPLIT_RANGES)
+    note(f"partial-tile issue order D={D} B=1 H=22 Sq=520 Skv=3000 P={len(SPLIT_RANGES)}")
+    out, lse = N.partition_attn(to_dev(w.q), to_dev(w.k), to_dev(w.v), w.ranges, w.scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.partition_states(w.q, w.k, w.v, w.ranges, w.scale)
+    check_states(out, lse, o_ref, l_ref, BF16_OUT, BF16_LSE, f"issue order D={D}")
+
+
 @pytest.mark.parametrize("D", [128, 64])
 def test_bf16_strided_inputs_and_guarded_outputs(D):
     """Non-contiguous q/k/v views and outputs followed by canaries that must stay untouched."""
