@@ -92,6 +92,21 @@ def equal_ranges(total: int, parts: int) -> List[Range]:
     return [(min(i * step, total), min((i + 1) * step, total)) for i in range(parts)]
 
 
+def random_ranges(seed: int, total: int, parts: int, max_len: int = 300) -> List[Range]:
+    """`parts` seeded ranges inside [0, total): random starts and lengths below max_len, every
+    17th one empty, every 23rd (from the 6th) a single key, the first one the whole sequence
+    (so that ranges overlap)."""
+    g = np.random.default_rng([seed, parts])
+    s = g.integers(0, total, size=parts)
+    n = g.integers(0, max_len, size=parts)
+    n[::17] = 0
+    n[5::23] = 1
+    e = np.minimum(s + n, total)
+    r = [(int(a), int(b)) for a, b in zip(s, e)]
+    r[0] = (0, total)
+    return r
+
+
 def nearest_partitions(P: int, local: int, count: int) -> List[int]:
     """The ``count`` partitions closest to ``local`` by |i - local|, ties to the lower index."""
     order = sorted(range(P), key=lambda i: (abs(i - local), i))

@@ -98,6 +98,26 @@ def test_grouped_states_and_partition_lse(D, fp8):
     check(out, lse, g_out, g_lse, f"grouped D={D} fp8={fp8}")
 
 
+@pytest.mark.parametrize("starts", [[0, 256], [0, 1, 1, 129, 256]])
+@pytest.mark.parametrize("D", [128, 64])
+def test_grouped_max_partitions(D, starts):
+    """AS_MAX_PARTITIONS (256) partitions in one launch: one group of all of them (the kernel's
+    table of a group's partitions full), or groups of 1, 0, 128 and 127; empty, single-key and
+    overlapping ranges among them. Composed states and every partition's LSE against the oracle."""
+    ranges = inputs.random_ranges(100 + D, 1500, N.AS_MAX_PARTITIONS)
+    note(f"grouped max partitions D={D} B=1 H=2 Sq=40 Skv=1500 P={len(ranges)} groups={starts}")
+    w = inputs.small_case(140 + D, 1, 2, 40, 1500, D, ranges)
+    out, lse, plse = N.partition_attn_grouped(dev(w.q), dev(w.k), dev(w.v), w.ranges, starts, w.scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.partition_states(w.q, w.k, w.v, w.ranges, w.scale)
+    got = plse.cpu().double().numpy()
+    fin = np.isfinite(l_ref)
+    assert np.array_equal(np.isneginf(got), ~fin)
+    assert np.abs(got[fin] - l_ref[fin]).max() <= LSE_TOL
+    g_out, g_lse = oracle_groups(o_ref, l_ref, starts)
+    check(out, lse, g_out, g_lse, f"grouped max partitions D={D} groups={starts}")
+
+
 @pytest.mark.parametrize("D", [128, 64])
 def test_grouped_fold_into_group_zero(D):
     """A given state composed into group 0's result (as the cached state at a reuse step)."""

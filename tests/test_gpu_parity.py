@@ -89,6 +89,20 @@ def test_partial_tiles_issued_on_their_own_compute_units(D):
 
 
 @pytest.mark.parametrize("D", [128, 64])
+def test_bf16_max_partitions(D):
+    """The largest number of partitions one launch takes (AS_MAX_PARTITIONS = 256; the ranges
+    travel in the kernel's arguments): empty, single-key and overlapping ranges among them,
+    a 40-row query shard (one partial query tile). Every element against the oracle."""
+    ranges = inputs.random_ranges(D, 1500, N.AS_MAX_PARTITIONS)
+    w = inputs.small_case(71 + D, 1, 2, 40, 1500, D, ranges)
+    note(f"bf16 max partitions D={D} B=1 H=2 Sq=40 Skv=1500 P={len(ranges)}")
+    out, lse = N.partition_attn(to_dev(w.q), to_dev(w.k), to_dev(w.v), w.ranges, w.scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.partition_states(w.q, w.k, w.v, w.ranges, w.scale)
+    check_states(out, lse, o_ref, l_ref, BF16_OUT, BF16_LSE, f"max partitions D={D}")
+
+
+@pytest.mark.parametrize("D", [128, 64])
 def test_bf16_strided_inputs_and_guarded_outputs(D):
     """Non-contiguous q/k/v views and outputs followed by canaries that must stay untouched."""
     B, H, Sq, Skv = 1, 2, 130, 333
