@@ -4,7 +4,8 @@
 //   Eq. 8: partition importance w(i, t) is the softmax over partitions of LSE_t(i).
 //
 // Launch 1: one thread per row (256 rows per workgroup); LSE[i][row] reads are
-// coalesced across threads (partition-major layout). Per row, M = max_i L_i and
+// coalesced across threads (partition-major layout); up to 32 partitions the row's LSE
+// values are read once into registers. Per row, M = max_i L_i and
 // S = sum_i e^(L_i - M) in index order, then w_i = e^(L_i - M) / S: differences
 // of nearby LSE values are exact, so w keeps fp32 accuracy whatever the size of
 // the LSE values (forming L* = M + ln S first would round L* to the ulp of M).
@@ -66,7 +67,13 @@ __device__ __forceinline__ float wave_sum(float x) {
 // e^(l - M) for l <= M (l = -inf gives 0)
 __device__ __forceinline__ float rel_exp(float l, float M) { return __builtin_amdgcn_exp2f((l - M) * kLog2e); }
 
+// PR > 0 (P <= PR): the row's P LSE values are loaded once, all in flight together, and
+// kept in registers (the loops over partitions are unrolled to PR with a predicate); PR = 0:
+// any P, each pass reading them again. The sums run in index order either way (the
+// register path adds exact zeros for i >= P), so both give the same bits.
+template <int PR>
 __global__ __launch_bounds__(kThreads) void contribution_rows_kernel(const ContribArgs a) {
+  static_assert(PR == 0 || PR <= kPB, "one LDS block of partitions");
   __shared__ float wt[kPB][kThreads + 1];   // w of one partition block, padded rows
   __shared__ float runs[8][kPB];
   const int g = blockIdx.x / a.chunks_per_group;
@@ -79,26 +86,48 @@ __global__ __launch_bounds__(kThreads) void contribution_rows_kernel(const Contr
   const float* lse = a.lse + row;   // LSE of partition i at lse[i * rows]
   const int P = a.P;
 
+  float L[PR > 0 ? PR : 1];
   float M = -INFINITY;
-  if (on) {
+  if constexpr (PR > 0) {
+#pragma unroll
+    for (int i = 0; i < PR; ++i) L[i] = (on && i < P) ? lse[i * rows] : -INFINITY;
+#pragma unroll
+    for (int i = 0; i < PR; ++i) M = fmaxf(M, L[i]);
+  } else if (on) {
 #pragma unroll 8
     for (int i = 0; i < P; ++i) M = fmaxf(M, lse[i * rows]);
   }
   const bool live = on && M != -INFINITY;
   float S = 0.f;
   if (live) {
+    if constexpr (PR > 0) {
+#pragma unroll
+      for (int i = 0; i < PR; ++i) S += rel_exp(L[i], M);
+    } else {
 #pragma unroll 8
-    for (int i = 0; i < P; ++i) S += rel_exp(lse[i * rows], M);
+      for (int i = 0; i < P; ++i) S += rel_exp(lse[i * rows], M);
+    }
   }
   const float inv = live ? 1.0f / S : 0.f;
 
   for (int i0 = 0; i0 < P; i0 += kPB) {
     const int nb = P - i0 < kPB ? P - i0 : kPB;
-    for (int j = 0; j < nb; ++j) {
-      const int64_t i = i0 + j;
-      const float w = live ? rel_exp(lse[i * rows], M) * inv : 0.f;
-      if (on && a.weights) a.weights[i * rows + row] = w;
-      wt[j][t] = w;
+    if constexpr (PR > 0) {
+#pragma unroll
+      for (int j = 0; j < PR; ++j) {
+        if (j < nb) {
+          const float w = live ? rel_exp(L[j], M) * inv : 0.f;
+          if (on && a.weights) a.weights[(int64_t)j * rows + row] = w;
+          wt[j][t] = w;
+        }
+      }
+    } else {
+      for (int j = 0; j < nb; ++j) {
+        const int64_t i = i0 + j;
+        const float w = live ? rel_exp(lse[i * rows], M) * inv : 0.f;
+        if (on && a.weights) a.weights[i * rows + row] = w;
+        wt[j][t] = w;
+      }
     }
     if (a.partial) {
       __syncthreads();
@@ -142,7 +171,9 @@ hipError_t launch_contribution(const ContribArgs& a, hipStream_t stream) {
   const int64_t blocks1 = G * a.chunks_per_group;
   if (blocks1 <= 0) return hipSuccess;
   if (blocks1 > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(contribution_rows_kernel, dim3((unsigned)blocks1), dim3(kThreads), 0, stream, a);
+  if (a.P <= 8) hipLaunchKernelGGL(contribution_rows_kernel<8>, dim3((unsigned)blocks1), dim3(kThreads), 0, stream, a);
+  else if (a.P <= kPB) hipLaunchKernelGGL(contribution_rows_kernel<kPB>, dim3((unsigned)blocks1), dim3(kThreads), 0, stream, a);
+  else hipLaunchKernelGGL(contribution_rows_kernel<0>, dim3((unsigned)blocks1), dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !a.scores) return e;
   const int64_t blocks2 = (G * a.P + 3) / 4;
