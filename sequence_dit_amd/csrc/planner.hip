@@ -9,7 +9,8 @@
 // nontemporal 16-byte loads. Differences and squares of fp32 inputs are exact in
 // fp64; only the sums round, and they are taken in a fixed order: per thread, then
 // a wave butterfly, then the four waves in index order, then the chunks of a slice
-// in index order. No atomics, so the norms are bitwise reproducible.
+// in a fixed order (eight lane-strided sums per lane, a tree, a butterfly). No atomics,
+// so the norms are bitwise reproducible.
 //
 // planner_decide_kernel / planner_epsilon_kernel: one workgroup, one thread per
 // partition (P <= 256); fp32 arithmetic on a few hundred scalars.
@@ -81,12 +82,21 @@ __global__ __launch_bounds__(kNormThreads) void state_norms_partial_kernel(const
   }
 }
 
-// One wave per slice: lane l adds the partials l, l + 64, ... in order, then a butterfly.
+// One wave per slice: lane l adds the partials l + 64 (8 m + k), k = 0..7, into eight sums
+// (so that eight loads are in flight, not one chain of dependent adds), m in order, then the
+// eight in a fixed tree, then a butterfly.
 __global__ __launch_bounds__(64) void state_norms_final_kernel(const NormArgs a) {
   const int p = blockIdx.x;
   const double* part = a.partial + (int64_t)p * a.chunks;
-  double s = 0.0;
-  for (int j = threadIdx.x; j < a.chunks; j += 64) s += part[j];
+  double t[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+  for (int j0 = threadIdx.x; j0 < a.chunks; j0 += 8 * 64) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int j = j0 + 64 * k;
+      t[k] += j < a.chunks ? part[j] : 0.0;
+    }
+  }
+  double s = ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
   s = wave_sum(s);
   if (threadIdx.x == 0) a.norms[p] = (float)sqrt(s);
 }
