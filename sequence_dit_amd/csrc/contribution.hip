@@ -68,9 +68,10 @@ __device__ __forceinline__ float wave_sum(float x) {
 __device__ __forceinline__ float rel_exp(float l, float M) { return __builtin_amdgcn_exp2f((l - M) * kLog2e); }
 
 // PR > 0 (P <= PR): the row's P LSE values are loaded once, all in flight together, and
-// kept in registers (the loops over partitions are unrolled to PR with a predicate); PR = 0:
-// any P, each pass reading them again. The sums run in index order either way (the
-// register path adds exact zeros for i >= P), so both give the same bits.
+// kept in registers (the loops over partitions are unrolled to PR with a predicate; the sum
+// runs in index order, adding exact zeros for i >= P). PR = 0 (any P): two passes over
+// blocks of kPB partitions, each block loaded together; the first keeps the running max and
+// a sum rescaled when a block moves it, the second gives the weights.
 template <int PR>
 __global__ __launch_bounds__(kThreads) void contribution_rows_kernel(const ContribArgs a) {
   static_assert(PR == 0 || PR <= kPB, "one LDS block of partitions");
@@ -93,19 +94,33 @@ __global__ __launch_bounds__(kThreads) void contribution_rows_kernel(const Contr
     for (int i = 0; i < PR; ++i) L[i] = (on && i < P) ? lse[i * rows] : -INFINITY;
 #pragma unroll
     for (int i = 0; i < PR; ++i) M = fmaxf(M, L[i]);
-  } else if (on) {
-#pragma unroll 8
-    for (int i = 0; i < P; ++i) M = fmaxf(M, lse[i * rows]);
+  }
+  float S = 0.f;
+  if constexpr (PR == 0) {
+    // blocks of kPB partitions, each block's LSE values loaded together; the max and the sum
+    // run over the blocks in one pass, the sum rescaled when a block moves the max
+    if (on) {
+      for (int i0 = 0; i0 < P; i0 += kPB) {
+        float X[kPB];
+#pragma unroll
+        for (int j = 0; j < kPB; ++j) X[j] = i0 + j < P ? lse[(int64_t)(i0 + j) * rows] : -INFINITY;
+        float mb = M;
+#pragma unroll
+        for (int j = 0; j < kPB; ++j) mb = fmaxf(mb, X[j]);
+        if (mb != -INFINITY) {
+          S *= rel_exp(M, mb);   // 1 when the max stays, 0 before the first finite value
+          M = mb;
+#pragma unroll
+          for (int j = 0; j < kPB; ++j) S += rel_exp(X[j], M);
+        }
+      }
+    }
   }
   const bool live = on && M != -INFINITY;
-  float S = 0.f;
-  if (live) {
-    if constexpr (PR > 0) {
+  if constexpr (PR > 0) {
+    if (live) {
 #pragma unroll
       for (int i = 0; i < PR; ++i) S += rel_exp(L[i], M);
-    } else {
-#pragma unroll 8
-      for (int i = 0; i < P; ++i) S += rel_exp(lse[i * rows], M);
     }
   }
   const float inv = live ? 1.0f / S : 0.f;
@@ -122,11 +137,16 @@ __global__ __launch_bounds__(kThreads) void contribution_rows_kernel(const Contr
         }
       }
     } else {
-      for (int j = 0; j < nb; ++j) {
-        const int64_t i = i0 + j;
-        const float w = live ? rel_exp(lse[i * rows], M) * inv : 0.f;
-        if (on && a.weights) a.weights[i * rows + row] = w;
-        wt[j][t] = w;
+      float X[kPB];
+#pragma unroll
+      for (int j = 0; j < kPB; ++j) X[j] = (live && j < nb) ? lse[(int64_t)(i0 + j) * rows] : -INFINITY;
+#pragma unroll
+      for (int j = 0; j < kPB; ++j) {
+        if (j < nb) {
+          const float w = live ? rel_exp(X[j], M) * inv : 0.f;
+          if (on && a.weights) a.weights[(int64_t)(i0 + j) * rows + row] = w;
+          wt[j][t] = w;
+        }
       }
     }
     if (a.partial) {
