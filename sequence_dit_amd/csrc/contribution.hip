@@ -5,8 +5,9 @@
 //
 // Launch 1: one thread per row (256 rows per workgroup); LSE[i][row] reads are
 // coalesced across threads (partition-major layout); up to 32 partitions the row's LSE
-// values are read once into registers. Per row, M = max_i L_i and
-// S = sum_i e^(L_i - M) in index order, then w_i = e^(L_i - M) / S: differences
+// values are read once into registers, above that in blocks of 32 (two passes). Per row,
+// M = max_i L_i and S = sum_i e^(L_i - M) (in index order up to 32 partitions; above, per
+// block, rescaled when a block moves the max), then w_i = e^(L_i - M) / S: differences
 // of nearby LSE values are exact, so w keeps fp32 accuracy whatever the size of
 // the LSE values (forming L* = M + ln S first would round L* to the ulp of M).
 // w is optionally written; for scores, the w of 32 partitions x 256 rows go
