@@ -578,7 +578,8 @@ def test_merge_tree_equals_flat_on_gpu():
 # contribution
 # --------------------------------------------------------------------------- #
 
-@pytest.mark.parametrize("P,rows,rpg", [(32, 2 * 3840, 3840), (5, 1000, 250), (8, 777, 777), (3, 64, 1), (256, 300, 100)])
+@pytest.mark.parametrize("P,rows,rpg", [(32, 2 * 3840, 3840), (5, 1000, 250), (8, 777, 777), (3, 64, 1), (256, 300, 100),
+                                        (33, 500, 250), (100, 257, 257)])
 def test_contribution_matches_oracle(P, rows, rpg):
     g = np.random.default_rng(P * 7 + rows)
     lse = (g.standard_normal((P, rows)) * 6).astype(np.float32)
